@@ -1,0 +1,196 @@
+"""CPU oracle for the batch-invariant forward path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product (the HIP library and its
+Python binding) never imports, links or calls anything here, and this package
+never imports the product: the two share only the seeded input bits.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, one final
+rounding); this module only builds it with gcc and marshals numpy arrays.
+Every function documents the passage of the pages it follows; the C file
+states the formulas.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.environ.get("BI_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (OpenMP over independent rows)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off",
+               "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I32 = ctypes.c_int32
+    D = ctypes.c_double
+    lib.or_round_bf16.argtypes = [P, P, I64]
+    lib.or_bf16_to_f64.argtypes = [P, P, I64]
+    lib.or_rmsnorm.argtypes = [P, I64, P, P, I64, P, I64, I64, D]
+    lib.or_rmsnorm_f64.argtypes = [P, I64, P, P, I64, P, I64, I64, D]
+    lib.or_matmul.argtypes = [P, I64, P, I64, P, I64, ctypes.c_int, I64, I64, I64]
+    lib.or_matmul_f64.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64]
+    lib.or_attention.argtypes = [P, I64, P, P, P, I64, I32, I32, I32, D, P, P, P]
+    lib.or_argmax.argtypes = [P, I64, I64, I64, P]
+    lib.or_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError(f"expected bf16 bit patterns as uint16, got {a.dtype}")
+    return a
+
+
+def num_threads() -> int:
+    return int(_load().or_num_threads())
+
+
+# --------------------------------------------------------------------------
+# bf16 conversion (the oracle's own, independent of numpy's float32 path)
+# --------------------------------------------------------------------------
+
+def round_bf16(x) -> np.ndarray:
+    """Round doubles straight to bf16 bit patterns, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().or_round_bf16(_p(x), _p(out), x.size)
+    return out
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    bits = _u16(bits)
+    out = np.empty(bits.shape, dtype=np.float64)
+    _load().or_bf16_to_f64(_p(bits), _p(out), bits.size)
+    return out
+
+
+# --------------------------------------------------------------------------
+# RMSNorm -- table row "RMSNorm", post "Defeating Nondeterminism in LLM
+# Inference の技術的なポイント" (mobiles-han.blogspot.com), section
+# 対応策：バッチ不変なカーネル設計.  Formula: Llama convention (see oracle.c).
+# --------------------------------------------------------------------------
+
+def rmsnorm(x, w, eps: float):
+    """x [M,H] bf16 bits, w [H] -> (y [M,H] bf16 bits, rstd [M] float32)."""
+    x = _u16(x); w = _u16(w)
+    M, H = x.shape
+    y = np.empty((M, H), dtype=np.uint16)
+    rstd = np.empty(M, dtype=np.float32)
+    _load().or_rmsnorm(_p(x), H, _p(w), _p(y), H, _p(rstd), M, H, float(eps))
+    return y, rstd
+
+
+def rmsnorm_f64(x, w, eps: float):
+    """Unrounded twin: (y [M,H] float64, rstd [M] float64)."""
+    x = _u16(x); w = _u16(w)
+    M, H = x.shape
+    y = np.empty((M, H), dtype=np.float64)
+    rstd = np.empty(M, dtype=np.float64)
+    _load().or_rmsnorm_f64(_p(x), H, _p(w), _p(y), H, _p(rstd), M, H, float(eps))
+    return y, rstd
+
+
+# --------------------------------------------------------------------------
+# Matmul -- table row 行列乗算（MatMul）, same section.  wt is the weight
+# stored [N,K] (transposed, K-contiguous); the product is x @ wt.T.
+# --------------------------------------------------------------------------
+
+def matmul(a, wt, out: str = "bf16"):
+    a = _u16(a); wt = _u16(wt)
+    M, K = a.shape
+    N, K2 = wt.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if out == "bf16":
+        c = np.empty((M, N), dtype=np.uint16); f32 = 0
+    elif out == "f32":
+        c = np.empty((M, N), dtype=np.float32); f32 = 1
+    else:
+        raise ValueError(out)
+    _load().or_matmul(_p(a), K, _p(wt), K, _p(c), N, f32, M, N, K)
+    return c
+
+
+def matmul_f64(a, wt):
+    a = _u16(a); wt = _u16(wt)
+    M, K = a.shape
+    N, K2 = wt.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    c = np.empty((M, N), dtype=np.float64)
+    _load().or_matmul_f64(_p(a), K, _p(wt), K, _p(c), N, M, N, K)
+    return c
+
+
+# --------------------------------------------------------------------------
+# Attention -- table row アテンション (Attention), same section; cache and
+# fresh tokens form one key sequence as in the FixedAttention sketch of the
+# post 「非決定モード → 決定モード」に切り替える例, section 注意点・補足実装.
+# --------------------------------------------------------------------------
+
+def attention(q, q_pos, k, v, scale: float):
+    """Causal attention over one sequence in logical order.
+
+    q [T,Hq,D], k/v [L,Hkv,D] bf16 bits; q_pos [T] absolute positions.
+    Returns (out bf16 bits [T,Hq,D], out float64 [T,Hq,D]).
+    """
+    q = _u16(q); k = _u16(k); v = _u16(v)
+    T, Hq, D = q.shape
+    L, Hkv, D2 = k.shape
+    if D2 != D or v.shape != k.shape or Hq % Hkv or D > 1024:
+        raise ValueError("bad attention shapes")
+    q_pos = np.ascontiguousarray(q_pos, dtype=np.int32)
+    if q_pos.shape != (T,) or (T and (q_pos.min() < 0 or q_pos.max() >= L)):
+        raise ValueError("q_pos must lie in [0, L)")
+    scratch = np.empty(max(1, T * Hq * L), dtype=np.float64)
+    o64 = np.empty((T, Hq, D), dtype=np.float64)
+    o16 = np.empty((T, Hq, D), dtype=np.uint16)
+    _load().or_attention(_p(q), T, _p(q_pos), _p(k), _p(v), L, Hq, Hkv, D,
+                         float(scale), _p(scratch), _p(o64), _p(o16))
+    return o16, o64
+
+
+# --------------------------------------------------------------------------
+# Greedy choice -- page "la température zéro n'est pas déterministe",
+# section "Le mensonge de la température zéro": argmax at every step.
+# --------------------------------------------------------------------------
+
+def argmax(logits):
+    """logits [rows,V] float32 -> ids [rows] int32; ties -> lowest index; NaN -> -1."""
+    x = np.ascontiguousarray(logits, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    rows, V = x.shape
+    ids = np.empty(rows, dtype=np.int32)
+    _load().or_argmax(_p(x), V, rows, V, _p(ids))
+    return ids

@@ -1,0 +1,274 @@
+/*
+ * oracle.c -- plain, slow, obviously-correct CPU reference for the
+ * batch-invariant forward path (RMSNorm, dense matmul, causal attention,
+ * greedy argmax and the toy decoder forward built from them).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or constant with
+ * the HIP library; the only thing both sides see is the seeded input bits.
+ *
+ * What it computes.  The method on the pages (the post "Defeating
+ * Nondeterminism in LLM Inference の技術的なポイント", mobiles-han.blogspot.com,
+ * section 対応策：バッチ不変なカーネル設計, and the matching table in the post
+ * "元OpenAIの研究者ら、AIの応答が毎回違う理由をついに解明", section
+ * 解決へのアプローチ) changes only *which* fixed rounding order each row gets;
+ * every op still computes an exact mathematical result up to rounding.  So the
+ * oracle is that exact definition: products of bf16 values are exact in
+ * double, every sum is a plain left-to-right double sum, and a single
+ * round-to-nearest-even to bf16 happens at the very end.  No tiling, no
+ * splitting, no fused reordering.
+ *
+ * Rows are independent; OpenMP parallelises over rows only and each row is a
+ * sequential loop, so the result does not depend on the thread count.
+ *
+ * Every function that returns rounded data also has a double-precision twin
+ * (suffix _f64) so a test can measure the error of a GPU result against the
+ * unrounded value.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#if defined(_OPENMP)
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* bf16 <-> double.  bf16 is the top half of an IEEE binary32.               */
+/* ------------------------------------------------------------------------ */
+
+static double bf16_bits_to_double(uint16_t h)
+{
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f; /* exact */
+}
+
+static uint16_t float_bits_top(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/*
+ * Round a double straight to bf16 (8 significant bits, binary32 exponent
+ * range), ties to even.  Done on the value, not the bits: scale so that the
+ * 8 kept bits sit left of the binary point, round with nearbyint() (default
+ * mode = ties-to-even), scale back.  Below 2^-126 the spacing is the fixed
+ * subnormal quantum 2^-133.  NaN stays NaN (quiet), overflow goes to inf.
+ */
+static uint16_t double_to_bf16(double x)
+{
+    if (isnan(x)) return (uint16_t)(signbit(x) ? 0xFFC0u : 0x7FC0u);
+    if (isinf(x) || x == 0.0) return float_bits_top((float)x); /* exact */
+    int e;
+    (void)frexp(x, &e);            /* |x| = f * 2^e, 0.5 <= f < 1           */
+    int q = e - 8;                 /* quantum exponent for 8 significant bits */
+    if (q < -133) q = -133;        /* bf16/binary32 subnormal quantum         */
+    double r = ldexp(nearbyint(ldexp(x, -q)), q);
+    if (fabs(r) >= 0x1p128) return (uint16_t)(signbit(x) ? 0xFF80u : 0x7F80u);
+    return float_bits_top((float)r); /* r is exact in binary32 and in bf16  */
+}
+
+void or_round_bf16(const double* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = double_to_bf16(in[i]);
+}
+
+void or_bf16_to_f64(const uint16_t* in, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_bits_to_double(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm.  The pages name the op (table row "RMSNorm" in the sections      */
+/* cited above) but never write its formula; the oracle takes the usual      */
+/* Llama form: mean of squares over the row (divide by H), eps inside the    */
+/* square root, elementwise weight w multiplies:                             */
+/*     rstd = 1 / sqrt( (1/H) * sum_j x_j^2 + eps )                          */
+/*     y_j  = x_j * rstd * w_j                                               */
+/* ------------------------------------------------------------------------ */
+
+void or_rmsnorm_f64(const uint16_t* x, int64_t ldx, const uint16_t* w,
+                    double* y, int64_t ldy, double* rstd,
+                    int64_t M, int64_t H, double eps)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* xr = x + m * ldx;
+        double ss = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            double v = bf16_bits_to_double(xr[j]);
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)H + eps);
+        if (rstd) rstd[m] = r;
+        if (y) {
+            for (int64_t j = 0; j < H; ++j)
+                y[m * ldy + j] = bf16_bits_to_double(xr[j]) * r * bf16_bits_to_double(w[j]);
+        }
+    }
+}
+
+void or_rmsnorm(const uint16_t* x, int64_t ldx, const uint16_t* w,
+                uint16_t* y, int64_t ldy, float* rstd,
+                int64_t M, int64_t H, double eps)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* xr = x + m * ldx;
+        double ss = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            double v = bf16_bits_to_double(xr[j]);
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)H + eps);
+        if (rstd) rstd[m] = (float)r;
+        for (int64_t j = 0; j < H; ++j)
+            y[m * ldy + j] = double_to_bf16(bf16_bits_to_double(xr[j]) * r *
+                                            bf16_bits_to_double(w[j]));
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dense matmul (table row 行列乗算（MatMul） in the sections cited above):  */
+/*     C[m][n] = sum_k A[m][k] * W[k][n]                                     */
+/* The logical weight is W[K][N]; it is stored transposed, Wt[n][k], the     */
+/* K-contiguous layout of a linear layer.  Products of two bf16 values are   */
+/* exact in double; the sum over k runs k = 0, 1, ..., K-1.                  */
+/* ------------------------------------------------------------------------ */
+
+void or_matmul_f64(const uint16_t* a, int64_t lda, const uint16_t* wt, int64_t ldw,
+                   double* c, int64_t ldc, int64_t M, int64_t N, int64_t K)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* ar = a + m * lda;
+        for (int64_t n = 0; n < N; ++n) {
+            const uint16_t* wr = wt + n * ldw;
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s += bf16_bits_to_double(ar[k]) * bf16_bits_to_double(wr[k]);
+            c[m * ldc + n] = s;
+        }
+    }
+}
+
+/* c_f32 != 0: C is float (one rounding double -> binary32);
+ * c_f32 == 0: C is bf16 (one rounding double -> bf16). */
+void or_matmul(const uint16_t* a, int64_t lda, const uint16_t* wt, int64_t ldw,
+               void* c, int64_t ldc, int c_f32, int64_t M, int64_t N, int64_t K)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* ar = a + m * lda;
+        for (int64_t n = 0; n < N; ++n) {
+            const uint16_t* wr = wt + n * ldw;
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s += bf16_bits_to_double(ar[k]) * bf16_bits_to_double(wr[k]);
+            if (c_f32) ((float*)c)[m * ldc + n] = (float)s;
+            else       ((uint16_t*)c)[m * ldc + n] = double_to_bf16(s);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Causal attention over one sequence (table row アテンション (Attention) in  */
+/* the sections cited above; the cache and the fresh tokens form one         */
+/* sequence of keys, as the FixedAttention sketch in the post                */
+/* 「非決定モード → 決定モード」に切り替える例 merges them before attending).   */
+/*                                                                           */
+/*   q   [T][Hq][D]   bf16, query rows; q_pos[t] = absolute position of row t */
+/*   k,v [L][Hkv][D]  bf16, keys/values in logical order 0..L-1              */
+/*   out [T][Hq][D]                                                          */
+/* Query head h reads KV head h / (Hq/Hkv).  Row t sees keys j = 0..q_pos[t]. */
+/*   s_j = scale * sum_d q[d] k_j[d]                                         */
+/*   out = sum_j exp(s_j - max s) v_j / sum_j exp(s_j - max s)               */
+/* The max shift changes nothing mathematically; it only keeps exp finite.   */
+/* Decode is the special case T = 1, q_pos = L - 1.                          */
+/* ------------------------------------------------------------------------ */
+
+static void attention_row(const uint16_t* qr, const uint16_t* k, const uint16_t* v,
+                          int64_t nvis, int32_t Hkv, int32_t D, int32_t g,
+                          double scale, double* s, double* o)
+{
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < nvis; ++j) {
+        const uint16_t* kr = k + (j * Hkv + g) * (int64_t)D;
+        double dot = 0.0;
+        for (int32_t d = 0; d < D; ++d)
+            dot += bf16_bits_to_double(qr[d]) * bf16_bits_to_double(kr[d]);
+        s[j] = scale * dot;
+        if (s[j] > mx) mx = s[j];
+    }
+    double z = 0.0;
+    for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+        double e = exp(s[j] - mx);
+        z += e;
+        const uint16_t* vr = v + (j * Hkv + g) * (int64_t)D;
+        for (int32_t d = 0; d < D; ++d) o[d] += e * bf16_bits_to_double(vr[d]);
+    }
+    for (int32_t d = 0; d < D; ++d) o[d] /= z;
+}
+
+/* scratch_scores: caller provides T*Hq*L doubles (one L-slice per row), so
+ * the oracle itself never allocates.  D <= 1024.  out_f64 and out_bf16 may
+ * each be NULL. */
+void or_attention(const uint16_t* q, int64_t T, const int32_t* q_pos,
+                  const uint16_t* k, const uint16_t* v, int64_t L,
+                  int32_t Hq, int32_t Hkv, int32_t D, double scale,
+                  double* scratch_scores, double* out_f64, uint16_t* out_bf16)
+{
+    int32_t group = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < Hq; ++h) {
+            int64_t nvis = (int64_t)q_pos[t] + 1;
+            if (nvis > L) nvis = L;
+            double* s = scratch_scores + (t * Hq + h) * L;
+            double o[1024];
+            attention_row(q + (t * Hq + h) * (int64_t)D, k, v, nvis, Hkv, D,
+                          h / group, scale, s, o);
+            for (int32_t d = 0; d < D; ++d) {
+                int64_t idx = (t * Hq + h) * (int64_t)D + d;
+                if (out_f64) out_f64[idx] = o[d];
+                if (out_bf16) out_bf16[idx] = double_to_bf16(o[d]);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Greedy choice (temperature 0 means taking the argmax at every step, page  */
+/* "la température zéro n'est pas déterministe", section "Le mensonge de la  */
+/* température zéro").  Ties go to the lowest index.  A NaN anywhere in the  */
+/* row gives -1.                                                             */
+/* ------------------------------------------------------------------------ */
+
+void or_argmax(const float* logits, int64_t ld, int64_t rows, int64_t V, int32_t* ids)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* x = logits + r * ld;
+        int32_t best = -1;
+        float bv = 0.0f;
+        for (int64_t i = 0; i < V; ++i) {
+            if (isnan(x[i])) { best = -1; break; }
+            if (best < 0 || x[i] > bv) { best = (int32_t)i; bv = x[i]; }
+        }
+        ids[r] = best;
+    }
+}
+
+int or_num_threads(void)
+{
+#if defined(_OPENMP)
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

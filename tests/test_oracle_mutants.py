@@ -1,0 +1,45 @@
+"""The oracle pins have teeth: each planted mistake in a copy of the oracle's
+C source (built on the CPU into a temporary library) must make the pin suite
+fail.  Only the oracle is mutated; nothing here touches a GPU."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "mean_over_H_minus_1": ("ss / (double)H", "ss / (double)(H - 1)"),
+    "eps_outside_root": ("sqrt(ss / (double)H + eps)", "sqrt(ss / (double)H) + eps"),
+    "rmsnorm_divides_by_rstd": ("bf16_bits_to_double(xr[j]) * r *", "bf16_bits_to_double(xr[j]) / r *"),
+    "matmul_drops_last_term": ("for (int64_t k = 0; k < K; ++k)", "for (int64_t k = 0; k + 1 < K; ++k)"),
+    "matmul_transposed_weight": ("bf16_bits_to_double(wr[k])", "bf16_bits_to_double(wt[(k % N) * ldw + n % K])"),
+    "attention_no_scale": ("s[j] = scale * dot;", "s[j] = dot;"),
+    "attention_wrong_group": ("h / group, scale", "h % Hkv, scale"),
+    "attention_sees_one_future_key": ("int64_t nvis = (int64_t)q_pos[t] + 1;", "int64_t nvis = (int64_t)q_pos[t] + 2;"),
+    "rounding_ties_away": ("nearbyint(ldexp(x, -q))", "round(ldexp(x, -q))"),
+    "argmax_ties_highest": ("x[i] > bv", "x[i] >= bv"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    n = src.count(old)
+    assert n >= 1, f"mutation anchor not found: {old}"
+    mutant = tmp_path / "oracle_mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(lib),
+                    str(mutant), "-lm"], check=True)
+    env = dict(os.environ, BI_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        "-k", "not thread_count"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
