@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-invariant forward path on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input:
+  1. projections (Llama-8B shapes): for every M in 1..64,128,256,...,2048:
+     RMSNorm [M,4096] -> bi_matmul [M,4096]x[4096,4096] -> bi_matmul
+     [M,4096]x[4096,14336]   (weights rotated over 3 copies, 432 MB > the
+     256 MB last-level cache, so weight reads come from HBM);
+  2. paged decode at 256 sequences, KV lengths log-uniform in [1, 32768]
+     (32/8 heads, head dim 128): bi_kv_append of the step's token + decode;
+  3. causal prefill of one 8192-token prompt.
+
+`value` (the headline) is the invariant GEMM throughput of phase 1: GEMM
+flops / wall time of phase 1 (HIP events bracketing the phase on the stream
+the kernels run on).  Decode GB/s and prefill TFLOP/s are reported beside it.
+The roofline entry is for the dominant kernel (bi_matmul): algorithmic flops
+(2MNK per launch) over the summed durations of its launches, from HIP events
+around each launch inside the timed steps.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "invariant GEMM TFLOP/s + decode-attn HBM GB/s (% roofline), M=1..2048"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+N_WEIGHT_COPIES = 3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--skip", default="", help="comma list of phases to skip: decode,prefill")
+    return ap.parse_args()
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "invariant_bi_rmsnorm_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "gemm_llama_sweep_counters.json")
+    try:
+        with open(p) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != src_hash(kernel_src):
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from invariant_bi_rmsnorm_amd import inputs as I
+    from invariant_bi_rmsnorm_amd import ops
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ops.lib()
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    skip = set(s for s in args.skip.split(",") if s)
+
+    def d16(bits):
+        return torch.from_numpy(np.array(bits, dtype=np.uint16, copy=True).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ phase 1 data
+    log("setup: projection weights")
+    H = I.LLAMA_H
+    Ns = I.LLAMA_N
+    wn = d16(I.llama_norm_weight())
+    W = {N: [d16(I.llama_weight(N))] for N in Ns}
+    for N in Ns:
+        for _ in range(N_WEIGHT_COPIES - 1):
+            W[N].append(W[N][0].clone())
+    x = d16(I.llama_x(2048))
+    Mmax = max(I.M_SWEEP)
+    y = torch.empty((Mmax, H), dtype=torch.bfloat16, device=dev)
+    C = {N: torch.empty((Mmax, N), dtype=torch.bfloat16, device=dev) for N in Ns}
+    gemm_flops_step = sum(2 * M * N * H for M in I.M_SWEEP for N in Ns)
+
+    # ------------------------------------------------------------ phase 2 data
+    S_DEC = 256
+    if "decode" not in skip:
+        log("setup: paged decode cache")
+        g = np.random.default_rng([I.TAG_DECODE, 0, 0])
+        lens = I.loguniform_lengths(g, S_DEC)
+        table, nblk = I.block_tables(g, lens)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(3000)
+        kc = torch.randn((nblk, I.ATT_HKV, 16, I.ATT_D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        vc = torch.randn((nblk, I.ATT_HKV, I.ATT_D, 16), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        qd = d16(I.queries(I.TAG_DECODE, 0, S_DEC))
+        knew = d16(I.normal_bf16(g, (S_DEC, I.ATT_HKV, I.ATT_D)))
+        vnew = d16(I.normal_bf16(g, (S_DEC, I.ATT_HKV, I.ATT_D)))
+        slots = torch.from_numpy(np.array([I.slots_for(table[s], [lens[s] - 1])[0] for s in range(S_DEC)],
+                                          np.int32)).to(dev)
+        tbl = torch.from_numpy(table).to(dev)
+        lens_d = torch.from_numpy(lens).to(dev)
+        max_len = int(lens.max())
+        ws = torch.empty(ops.bi_attention_workspace_bytes(S_DEC, I.ATT_HQ, I.ATT_D, max_len) // 4 + 4,
+                         dtype=torch.float32, device=dev)
+        dec_out = torch.empty((S_DEC, I.ATT_HQ, I.ATT_D), dtype=torch.bfloat16, device=dev)
+        dec_bytes = (int(lens.sum()) * I.ATT_HKV * I.ATT_D * 2 * 2 + S_DEC * I.ATT_HQ * I.ATT_D * 2 * 2
+                     + 4 * int(sum(-(-int(L) // 16) for L in lens)))
+    # ------------------------------------------------------------ phase 3 data
+    P_PRE = 8192
+    if "prefill" not in skip:
+        log("setup: prefill prompt")
+        gp = np.random.default_rng([I.TAG_PREFILL, 0, 0])
+        ptable, pnblk = I.block_tables(gp, [P_PRE])
+        genp = torch.Generator(device=dev)
+        genp.manual_seed(4000)
+        pk = torch.randn((pnblk, I.ATT_HKV, 16, I.ATT_D), generator=genp, device=dev).to(torch.bfloat16)
+        pv = torch.randn((pnblk, I.ATT_HKV, I.ATT_D, 16), generator=genp, device=dev).to(torch.bfloat16)
+        pq = torch.randn((P_PRE, I.ATT_HQ, I.ATT_D), generator=genp, device=dev).to(torch.bfloat16)
+        ptbl = torch.from_numpy(ptable).to(dev)
+        pqs = torch.tensor([0, P_PRE], dtype=torch.int32, device=dev)
+        plens = torch.tensor([P_PRE], dtype=torch.int32, device=dev)
+        pout = torch.empty_like(pq)
+        pre_flops = 4 * I.ATT_HQ * I.ATT_D * (P_PRE * (P_PRE + 1) // 2)
+    scale = 1.0 / math.sqrt(I.ATT_D)
+
+    # ------------------------------------------------------------ one step
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    rec = {"gemm": [], "rms": [], "phase1": [], "decode": [], "prefill": []}
+    call = [0]
+
+    def step(record: bool):
+        p1s, p1e = E(), E()
+        p1s.record(stream)
+        for M in I.M_SWEEP:
+            if record:
+                rs, re_ = E(), E()
+                rs.record(stream)
+            ops.bi_rmsnorm(x[:M], wn, I.LLAMA_EPS, y=y[:M], want_rstd=False)
+            if record:
+                re_.record(stream)
+                rec["rms"].append((rs, re_, M))
+            for N in Ns:
+                wt = W[N][call[0] % N_WEIGHT_COPIES]
+                call[0] += 1
+                if record:
+                    gs, ge = E(), E()
+                    gs.record(stream)
+                ops.bi_matmul(y[:M], wt, c=C[N][:M])
+                if record:
+                    ge.record(stream)
+                    rec["gemm"].append((gs, ge, 2 * M * N * H, M, N))
+        p1e.record(stream)
+        if record:
+            rec["phase1"].append((p1s, p1e))
+        if "decode" not in skip:
+            ds, de = E(), E()
+            ds.record(stream)
+            ops.bi_kv_append(knew, vnew, slots, kc, vc)
+            ops.bi_attention_decode(qd, kc, vc, tbl, lens_d, max_len, scale, ws=ws, out=dec_out)
+            de.record(stream)
+            if record:
+                rec["decode"].append((ds, de))
+        if "prefill" not in skip:
+            ps, pe = E(), E()
+            ps.record(stream)
+            ops.bi_attention_prefill(pq, pqs, plens, pk, pv, ptbl, P_PRE, scale, out=pout)
+            pe.record(stream)
+            if record:
+                rec["prefill"].append((ps, pe))
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"timed {args.steps}")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    def total_ms(pairs):
+        return sum(a.elapsed_time(b) for a, b, *_ in pairs)
+
+    phase1_ms = total_ms(rec["phase1"]) / args.steps
+    value = gemm_flops_step / (phase1_ms * 1e-3) / 1e12
+    gemm_ms = total_ms(rec["gemm"])
+    gemm_flops = sum(r[2] for r in rec["gemm"])
+    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    n_launch = len(rec["gemm"])
+    traffic = traffic_from_profile("gemm.hip")
+
+    # per-M table (median over steps)
+    per = {}
+    for (a, b, fl, M, N) in rec["gemm"]:
+        per.setdefault((M, N), []).append(a.elapsed_time(b))
+    sweep = []
+    for (M, N), ts in sorted(per.items()):
+        t = float(np.median(ts)) * 1e-3
+        fl = 2 * M * N * H
+        byt = 2 * (M * H + N * H + M * N)
+        roof_t = max(fl / (PEAK_BF16_TFLOPS * 1e12), byt / (PEAK_HBM_GBS * 1e9))
+        sweep.append({"M": M, "N": N, "us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
+                      "frac_mfma_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "frac_roofline": round(roof_t / t, 4)})
+
+    rms_ms = total_ms(rec["rms"])
+    rms_bytes = sum(4 * M * H + 2 * H for (_, _, M) in rec["rms"])
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama8b-projection sweep (RMSNorm 4096 + bf16 GEMM 4096->4096 and 4096->14336, "
+                        "M=1..64,128,256,512,1024,2048) + paged decode S=256 + causal prefill 8192",
+            "M_sweep": list(I.M_SWEEP), "hidden": H, "N": list(Ns),
+            "gemm_tile": "128x128x64, v_mfma_f32_16x16x32_bf16, 4 waves",
+            "value_basis": "GEMM flops of the sweep / wall time of the projection phase",
+        },
+        "roofline": {
+            "kernel": "bi_matmul (gemm_kernel)",
+            "bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
+            "traffic": traffic,
+            "launches": n_launch, "avg_launch_us": round(gemm_ms * 1e3 / n_launch, 3),
+            "flops_per_launch_avg": gemm_flops / n_launch,
+        },
+        "gemm_sweep": sweep,
+        "rmsnorm": {"GB/s": round(rms_bytes / (rms_ms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(rms_bytes / (rms_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "note": "M=1..2048 rows of 4096, launch-latency bound at this size"},
+    }
+    if "decode" not in skip:
+        dms = total_ms(rec["decode"]) / args.steps
+        gbs = dec_bytes / (dms * 1e-3) / 1e9
+        result["decode_attn"] = {"S": S_DEC, "kv_tokens": int(lens.sum()), "max_len": max_len,
+                                 "us": round(dms * 1e3, 2), "GB/s": round(gbs, 1),
+                                 "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": dec_bytes,
+                                 "includes": "bi_kv_append + split kernel + combine kernel"}
+    if "prefill" not in skip:
+        pms = total_ms(rec["prefill"]) / args.steps
+        tf = pre_flops / (pms * 1e-3) / 1e12
+        result["prefill"] = {"P": P_PRE, "us": round(pms * 1e3, 1), "TFLOP/s": round(tf, 2),
+                             "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    # non-invariant vendor GEMM (hipBLASLt through torch) on the same sweep, context only
+    try:
+        torch.cuda.synchronize()
+        for rep in range(2):
+            bs, be = E(), E()
+            bs.record(stream)
+            for M in I.M_SWEEP:
+                for N in Ns:
+                    torch.nn.functional.linear(y[:M], W[N][call[0] % N_WEIGHT_COPIES], out=C[N][:M])
+                    call[0] += 1
+            be.record(stream)
+        torch.cuda.synchronize()
+        bms = bs.elapsed_time(be)
+        result["baseline_hipblaslt"] = {"TFLOP/s": round(gemm_flops_step / (bms * 1e-3) / 1e12, 3),
+                                        "note": "torch.nn.functional.linear on the same sweep (not batch-invariant)"}
+    except Exception as e:  # context only
+        result["baseline_hipblaslt"] = {"error": str(e)[:200]}
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        a = I.llama_x(2048)
+        wt = I.llama_weight(14336)
+        probe_rows = 8
+        t = time.perf_counter()
+        oracle.matmul(a[:probe_rows], wt)
+        dt = time.perf_counter() - t
+        rows = int(min(2048, max(probe_rows, probe_rows * args.cpu_seconds / max(dt, 1e-3))))
+        t = time.perf_counter()
+        oracle.matmul(a[:rows], wt)
+        dt = time.perf_counter() - t
+        fl = 2 * rows * 14336 * H
+        result["cpu_baseline"] = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": oracle.num_threads(), "kind": "oracle",
+                                  "sample": f"oracle matmul (fp64) of {rows} rows of the M=2048 "
+                                            f"[M,4096]x[4096,14336] GEMM, {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * bi.h -- C ABI of libbi.so: batch-invariant transformer forward kernels for
+ * AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * Batch invariance: for any one row (a token's activations, a query row of
+ * attention), the bits of the result do not depend on the batch size, on the
+ * row's position in the batch, on what else is in the batch, nor on the
+ * KV-cache state (cache hit or fresh, chunked or single-shot prefill, decode).
+ * The property and the three ops that need care are laid out in the post
+ * "論文／ブログ「Defeating Nondeterminism in LLM Inference」の技術的なポイント"
+ * (mobiles-han.blogspot.com, 2025-09-14 archive), sections
+ * "バッチ不変性 (Batch Invariance) の意味" (definition) and
+ * "対応策：バッチ不変なカーネル設計" (table: RMSNorm, MatMul, Attention).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - bf16 tensors are passed as void* to 16-bit storage (IEEE binary32 top
+ *    half); fp32 as float*; indices as int32_t*.  All tensor pointers are
+ *    DEVICE pointers unless stated otherwise, allocated and owned by the
+ *    caller.  The library never allocates, frees or keeps device memory, and
+ *    holds no mutable global state; it is safe to call from several threads.
+ *  - Leading dimensions (ld*) are in elements.  Row-major everywhere.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call is asynchronous on that stream.
+ *  - Return value: a bi_status.  Arguments are validated on the host, in full,
+ *    before anything is launched; on error nothing is launched and nothing is
+ *    written.  Device contents (lengths, block tables, slots) cannot be checked
+ *    on the host; the kernels bounds-check every index they read and never
+ *    access memory outside the buffers described by the size arguments
+ *    (an out-of-range index produces unspecified output values, not a fault).
+ *    Faults of an asynchronous launch surface at the caller's next
+ *    synchronisation.  No C++ exception crosses this ABI.
+ *  - Unsupported-but-valid shapes return BI_ERR_UNSUPPORTED; they are never
+ *    routed to a different kernel, because a shape-dependent kernel switch is
+ *    exactly what breaks batch invariance.
+ *  - M == 0 / T == 0 / S == 0 is a valid no-op.
+ */
+#ifndef BI_H
+#define BI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BI_ABI_VERSION 1
+
+typedef enum {
+    BI_OK = 0,
+    BI_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, ld too small, misaligned  */
+    BI_ERR_UNSUPPORTED = 2,        /* valid but outside the single kernel configuration       */
+    BI_ERR_WORKSPACE_TOO_SMALL = 3,
+    BI_ERR_NO_DEVICE = 4,
+    BI_ERR_LAUNCH = 5              /* hipGetLastError() reported a launch failure             */
+} bi_status;
+
+typedef enum { BI_BF16 = 0, BI_F32 = 1 } bi_dtype;
+
+/* Fixed strategy constants (compile-time properties of the one configuration). */
+#define BI_KV_BLOCK 16      /* tokens per KV-cache block                                 */
+#define BI_KV_SPLIT 256     /* tokens per attention split, aligned to absolute position 0 */
+#define BI_HEAD_DIM 128     /* the only supported head dimension                          */
+
+int         bi_abi_version(void);
+const char* bi_status_string(int status);
+
+/*
+ * RMSNorm, one row per workgroup with a fixed reduction order
+ * (table row "RMSNorm" of the section 対応策：バッチ不変なカーネル設計: keep a
+ * data-parallel strategy whatever the batch size so each row's reduction order
+ * never changes).
+ *
+ *   rstd[m] = 1 / sqrt( (1/H) * sum_j x[m][j]^2 + eps )     (fp32 accumulation)
+ *   y[m][j] = bf16( (x[m][j] * rstd[m]) * w[j] )             (fp32, one rounding to bf16)
+ *
+ * x   [M][ldx] bf16, w [H] bf16, y [M][ldy] bf16, rstd [M] fp32 or NULL.
+ * Requires H % 8 == 0, 8 <= H <= 16384, ldx % 8 == 0, ldy % 8 == 0, x/w/y 16-byte
+ * aligned.  y may alias x only if ldy == ldx (in-place).
+ */
+int bi_rmsnorm(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
+               float* rstd, int64_t M, int64_t H, float eps, void* stream);
+
+/*
+ * Dense matmul with one MFMA tile configuration for every shape
+ * (table row 行列乗算（MatMul） of the same section: one kernel configuration
+ * for all shapes, fixed tile size, no split-K, no switch of compute unit by size).
+ *
+ *   c[m][n] = sum_{k=0..K-1} a[m][k] * wt[n][k]     (fp32 accumulation, ascending k)
+ *
+ * a  [M][lda] bf16; wt [N][ldw] bf16 = the logical weight W[K][N] stored
+ * transposed (the K-contiguous layout of a linear layer); c [M][ldc], bf16
+ * (round to nearest even) or fp32 per c_dtype.
+ * Requires K % 64 == 0, N % 4 == 0, lda/ldw % 8 == 0, ldc % 4 == 0,
+ * a/wt 16-byte aligned, c 8-byte (bf16) / 16-byte (fp32) aligned.
+ */
+int bi_matmul(const void* a, int64_t lda, const void* wt, int64_t ldw,
+              void* c, int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K,
+              void* stream);
+
+/*
+ * Append fresh keys/values to the paged cache, so that attention reads cached
+ * and fresh tokens through one layout (table row アテンション (Attention) of the
+ * same section: merge cache and current data into one consistent layout before
+ * attending; the FixedAttention sketch of the post
+ * 「非決定モード → 決定モード」に切り替える例, section 注意点・補足実装).
+ *
+ * k_new, v_new: token t, head h, dim d at [t*ld_new + h*D + d] (bf16).
+ * slots [T]: slot = block*16 + offset of token t (int32); a slot outside
+ *   [0, num_blocks*16) is skipped.
+ * k_cache [num_blocks][Hkv][16][D] bf16 (token-major inside a block);
+ * v_cache [num_blocks][Hkv][D][16] bf16 (dim-major inside a block).
+ * Requires D == 128, ld_new >= Hkv*D, ld_new % 8 == 0, 16-byte aligned pointers.
+ * A bitwise copy; no arithmetic.
+ */
+int bi_kv_append(const void* k_new, const void* v_new, int64_t ld_new, const int32_t* slots,
+                 int64_t T, void* k_cache, void* v_cache, int64_t num_blocks,
+                 int32_t Hkv, int32_t D, void* stream);
+
+/*
+ * Workspace for bi_attention_decode: S * Hq * ceil(max_kv_len/256) split
+ * partials of (D + 2) floats each.
+ */
+size_t bi_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D, int32_t max_kv_len);
+
+/*
+ * Paged decode attention with FIXED-SIZE KV splits (same table row: use a fixed
+ * split size for Split-KV / FlashDecode, never a split count derived from the
+ * batch or the length).  One query token per sequence; the token's own K/V
+ * must already be in the cache (bi_kv_append), and kv_lens counts it.
+ *
+ * Split i of sequence s covers absolute tokens [256 i, 256 i + 256).  Per split
+ * and query head: split-local max, exp2 weights, their sum and the weighted
+ * values (fp32, into the workspace); then a left fold over splits 0,1,2,...
+ * For the same query row and the same cached K/V the result is bitwise equal
+ * to row (kv_len - 1) of bi_attention_prefill.
+ *
+ * q [S rows][ldq] bf16, row s holds Hq heads of D; out likewise with ldo.
+ * block_table [S][max_blocks] int32 physical block ids; kv_lens [S] int32 in
+ * [1, max_kv_len] and <= max_blocks*16.  scale multiplies q.k (1/sqrt(D) usually).
+ * ws: device workspace of at least bi_attention_workspace_bytes(S, Hq, D, max_kv_len).
+ * Requires D == 128, Hq % Hkv == 0, Hq/Hkv <= 16, 1 <= max_kv_len <= 1<<20,
+ * S <= 8192, 16-byte aligned q/out/caches, ldq/ldo % 8 == 0.
+ */
+int bi_attention_decode(const void* q, int64_t ldq, const void* k_cache, const void* v_cache,
+                        int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                        const int32_t* kv_lens, void* out, int64_t ldo,
+                        int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_kv_len,
+                        float scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Causal (chunked) prefill attention over the paged cache (same table row:
+ * chunked prefill must not change the reduction path).  Sequence s contributes
+ * T_s = q_start[s+1] - q_start[s] query tokens, which sit at absolute positions
+ * [kv_lens[s] - T_s, kv_lens[s]) and whose K/V are already in the cache.  A query
+ * at position p sees keys 0..p.  Splits are the same absolute 256-token splits
+ * as decode, so the output of a row does not depend on how the prompt was
+ * chunked, on what else is in the call, nor on whether the row is computed
+ * here or by bi_attention_decode.
+ *
+ * q [T][ldq] bf16 (rows ordered by q_start), out [T][ldo] bf16;
+ * q_start [S+1] int32 ascending with q_start[0] == 0 and q_start[S] == T;
+ * kv_lens [S] int32; max_q_len >= every T_s (host-side bound for the grid).
+ * Requires D == 128, Hq % Hkv == 0, Hq/Hkv in {1,2,4,8,16}.
+ */
+int bi_attention_prefill(const void* q, int64_t ldq, const int32_t* q_start,
+                         const int32_t* kv_lens, const void* k_cache, const void* v_cache,
+                         int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                         void* out, int64_t ldo, int32_t S, int64_t T, int32_t Hq,
+                         int32_t Hkv, int32_t D, int32_t max_q_len, float scale,
+                         void* stream);
+
+/*
+ * Greedy token choice (temperature 0 = argmax at every step; page
+ * "la température zéro n'est pas déterministe", section "Le mensonge de la
+ * température zéro").  ids[r] = index of the largest logit of row r, ties to
+ * the lowest index, -1 if the row holds a NaN.  logits [rows][ld] fp32.
+ */
+int bi_argmax(const float* logits, int64_t ld, int64_t rows, int64_t V, int32_t* ids,
+              void* stream);
+
+/*
+ * Diagnostic: one v_mfma_f32_16x16x32_bf16 on a [16][32] bf16 (row-major) and
+ * b [32][16] bf16 (row-major) into c [16][16] fp32 (row-major), with the
+ * operand/result lane layout the kernels assume.  The batch-invariance
+ * argument of bi_matmul and of attention rests on the fact that an MFMA
+ * result element depends only on its own row of a and column of b; tests use
+ * this entry point to check that and the layout.  Device pointers.
+ */
+int bi_probe_mfma_bf16(const void* a, const void* b, float* c, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BI_H */

@@ -1,0 +1,246 @@
+"""Thin Python binding of libbi.so (the C ABI in include/bi.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libbi.so.  PyTorch provides device memory (output tensors are
+allocated with torch when the caller does not pass them) and the current HIP
+stream.  There is no fallback: if libbi.so is missing or no GPU is present,
+calls raise.
+
+Tensor conventions: bf16 data as torch.bfloat16 device tensors, fp32 as
+torch.float32, indices as torch.int32, all contiguous in their last dimension.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("BI_LIB") or os.path.join(_HERE, "libbi.so")
+
+BI_OK = 0
+BI_ERR_INVALID_ARGUMENT = 1
+BI_ERR_UNSUPPORTED = 2
+BI_ERR_WORKSPACE_TOO_SMALL = 3
+BI_ERR_NO_DEVICE = 4
+BI_ERR_LAUNCH = 5
+BI_BF16 = 0
+BI_F32 = 1
+
+# (name, restype, argtypes) of every symbol declared in include/bi.h
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "bi_abi_version": (ctypes.c_int, []),
+    "bi_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "bi_rmsnorm": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _I64, _I64, _F, _P]),
+    "bi_matmul": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, ctypes.c_int, _I64, _I64, _I64, _P]),
+    "bi_kv_append": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _P, _I64, _I32, _I32, _P]),
+    "bi_attention_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "bi_attention_decode": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _I32, _P, _P, _I64,
+                                           _I32, _I32, _I32, _I32, _I32, _F, _P, _SZ, _P]),
+    "bi_attention_prefill": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _P, _I32, _P, _I64,
+                                            _I32, _I64, _I32, _I32, _I32, _I32, _F, _P]),
+    "bi_argmax": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
+    "bi_probe_mfma_bf16": (ctypes.c_int, [_P, _P, _P, _P]),
+}
+
+_lib = None
+
+
+class BiError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({status_string(status)})")
+
+
+def lib():
+    """Load libbi.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"libbi.so not found at {LIB_PATH}; build it with "
+                "`python -m invariant_bi_rmsnorm_amd._build` (there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().bi_status_string(int(s)).decode()
+
+
+def _check(status: int, fn: str):
+    if status != BI_OK:
+        raise BiError(status, fn)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() and t.stride(-1) != 1:
+        raise ValueError(f"{name} must be contiguous in its last dimension")
+
+
+def _row_stride(t: torch.Tensor, row_extent: int) -> int:
+    """Elements between consecutive rows; a one-row tensor may carry any stride
+    (torch keeps 0 or odd strides on size-1 dimensions), so use the row extent."""
+    if t.shape[0] <= 1:
+        return max(row_extent, 1)
+    return t.stride(0)
+
+
+def _ld(t: torch.Tensor) -> int:
+    return _row_stride(t, t.shape[1]) if t.dim() >= 2 else t.shape[-1]
+
+
+def abi_version() -> int:
+    return int(lib().bi_abi_version())
+
+
+# ---------------------------------------------------------------------------
+def bi_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float, y: torch.Tensor = None,
+               rstd: torch.Tensor = None, want_rstd: bool = True, stream=None):
+    _need(x, torch.bfloat16, "x"); _need(w, torch.bfloat16, "w")
+    M, H = x.shape
+    if y is None:
+        y = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    if rstd is None and want_rstd:
+        rstd = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().bi_rmsnorm(_ptr(x), _ld(x), _ptr(w), _ptr(y), _ld(y), _ptr(rstd), M, H,
+                            float(eps), _stream(stream)), "bi_rmsnorm")
+    return y, rstd
+
+
+def bi_matmul(a: torch.Tensor, wt: torch.Tensor, out_dtype=torch.bfloat16, c: torch.Tensor = None,
+              stream=None) -> torch.Tensor:
+    """c = a @ wt.T with wt stored [N, K]."""
+    _need(a, torch.bfloat16, "a"); _need(wt, torch.bfloat16, "wt")
+    M, K = a.shape
+    N, K2 = wt.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    code = BI_BF16 if c.dtype == torch.bfloat16 else BI_F32 if c.dtype == torch.float32 else None
+    if code is None:
+        raise ValueError("c must be bfloat16 or float32")
+    _check(lib().bi_matmul(_ptr(a), _ld(a), _ptr(wt), _ld(wt), _ptr(c), _ld(c), code, M, N, K,
+                           _stream(stream)), "bi_matmul")
+    return c
+
+
+def bi_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slots: torch.Tensor,
+                 k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None):
+    """k_new/v_new [T, Hkv, D] (rows may be strided views of a wider tensor)."""
+    T, Hkv, D = k_new.shape
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, torch.bfloat16, n)
+        if t.numel() and (t.stride(2) != 1 or (Hkv > 1 and t.stride(1) != D)):
+            raise ValueError(f"{n}: heads must be contiguous [Hkv, D] inside a token row")
+    ld = _row_stride(k_new, Hkv * D)
+    if ld != _row_stride(v_new, Hkv * D):
+        raise ValueError("k_new and v_new must share the row stride")
+    _need(slots, torch.int32, "slots")
+    num_blocks = k_cache.shape[0]
+    _check(lib().bi_kv_append(_ptr(k_new), _ptr(v_new), ld, _ptr(slots), T,
+                              _ptr(k_cache), _ptr(v_cache), num_blocks, Hkv, D, _stream(stream)),
+           "bi_kv_append")
+
+
+def bi_attention_workspace_bytes(S: int, Hq: int, D: int, max_kv_len: int) -> int:
+    return int(lib().bi_attention_workspace_bytes(S, Hq, D, max_kv_len))
+
+
+def _heads_view(q: torch.Tensor, name: str):
+    """[rows, H, D] view whose heads are contiguous inside a row; returns (H, D, ld)."""
+    _need(q, torch.bfloat16, name)
+    if q.dim() != 3:
+        raise ValueError(f"{name} must be [rows, heads, head_dim]")
+    rows, H, D = q.shape
+    if q.numel() and (q.stride(2) != 1 or (H > 1 and q.stride(1) != D)):
+        raise ValueError(f"{name}: heads must be contiguous [H, D] inside a row")
+    return H, D, _row_stride(q, H * D)
+
+
+def bi_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        block_table: torch.Tensor, kv_lens: torch.Tensor, max_kv_len: int,
+                        scale: float, ws: torch.Tensor = None, out: torch.Tensor = None,
+                        stream=None) -> torch.Tensor:
+    """q [S, Hq, D] (rows may be strided); k_cache [nblk, Hkv, 16, D]; returns out [S, Hq, D]."""
+    S = q.shape[0]
+    Hq, D, ldq = _heads_view(q, "q")
+    Hkv = k_cache.shape[1]
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _, _, ldo = _heads_view(out, "out")
+    need = bi_attention_workspace_bytes(S, Hq, D, max_kv_len)
+    if ws is None:
+        ws = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=q.device)
+    _check(lib().bi_attention_decode(_ptr(q), ldq, _ptr(k_cache), _ptr(v_cache),
+                                     k_cache.shape[0], _ptr(block_table), block_table.shape[1],
+                                     _ptr(kv_lens), _ptr(out), ldo, S, Hq, Hkv, D,
+                                     int(max_kv_len), float(scale), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)),
+           "bi_attention_decode")
+    return out
+
+
+def bi_attention_prefill(q: torch.Tensor, q_start: torch.Tensor, kv_lens: torch.Tensor,
+                         k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                         max_q_len: int, scale: float, out: torch.Tensor = None,
+                         stream=None) -> torch.Tensor:
+    """q [T, Hq, D] (rows may be strided), rows grouped by q_start [S+1]; returns out [T, Hq, D]."""
+    T = q.shape[0]
+    Hq, D, ldq = _heads_view(q, "q")
+    Hkv = k_cache.shape[1]
+    S = q_start.shape[0] - 1
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _, _, ldo = _heads_view(out, "out")
+    _check(lib().bi_attention_prefill(_ptr(q), ldq, _ptr(q_start), _ptr(kv_lens),
+                                      _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
+                                      _ptr(block_table), block_table.shape[1], _ptr(out), ldo,
+                                      S, T, Hq, Hkv, D, int(max_q_len), float(scale),
+                                      _stream(stream)), "bi_attention_prefill")
+    return out
+
+
+def bi_argmax(logits: torch.Tensor, ids: torch.Tensor = None, stream=None) -> torch.Tensor:
+    _need(logits, torch.float32, "logits")
+    rows, V = logits.shape
+    if ids is None:
+        ids = torch.empty((rows,), dtype=torch.int32, device=logits.device)
+    _check(lib().bi_argmax(_ptr(logits), _ld(logits), rows, V, _ptr(ids), _stream(stream)),
+           "bi_argmax")
+    return ids
+
+
+def bi_probe_mfma_bf16(a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:
+    c = torch.empty((16, 16), dtype=torch.float32, device=a.device)
+    _check(lib().bi_probe_mfma_bf16(_ptr(a), _ptr(b), _ptr(c), _stream(stream)), "bi_probe_mfma_bf16")
+    return c

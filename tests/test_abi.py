@@ -1,0 +1,147 @@
+"""The C ABI: libbi.so builds for gfx950, loads, exports every symbol that
+include/bi.h declares, and its host-side validation rejects bad arguments
+before any launch (so these run without a GPU: no compute call is made)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bi.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bi_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from invariant_bi_rmsnorm_amd import ops
+    if not os.path.exists(ops.LIB_PATH):
+        from invariant_bi_rmsnorm_amd import _build
+        _build.build()
+    return ops.lib()
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for s in ("bi_rmsnorm", "bi_matmul", "bi_kv_append", "bi_attention_decode",
+              "bi_attention_prefill", "bi_attention_workspace_bytes", "bi_argmax"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(L):
+    from invariant_bi_rmsnorm_amd import ops
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(bi_[a-z0-9_]+)$", out, flags=re.M))
+    for s in declared_symbols():
+        assert s in exported, s
+        assert hasattr(L, s)
+    assert set(ops.SIGNATURES) == set(declared_symbols())
+
+
+def test_library_links_no_oracle_code(L):
+    from invariant_bi_rmsnorm_amd import ops
+    out = subprocess.run(["nm", "-D", ops.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert not re.search(r"\bor_(rmsnorm|matmul|attention|argmax)", out)
+    ldd = subprocess.run(["ldd", ops.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in ldd
+
+
+def test_gfx950_code_object_present():
+    from invariant_bi_rmsnorm_amd import ops
+    data = open(ops.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx[0-9a-z]+)", data))
+    assert targets == {b"gfx950"}
+
+
+def test_version_and_status_strings(L):
+    from invariant_bi_rmsnorm_amd import ops
+    assert ops.abi_version() == 1
+    assert ops.status_string(0) == "ok"
+    assert "unsupported" in ops.status_string(2)
+    assert ops.status_string(99) == "unknown status"
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    code = ("import os; os.environ['BI_LIB']='/nonexistent/libbi.so'\n"
+            "from invariant_bi_rmsnorm_amd import ops\n"
+            "try:\n    ops.lib()\nexcept RuntimeError as e:\n    print('RAISED', e)\n")
+    r = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert "RAISED" in r.stdout and "no fallback" in r.stdout
+
+
+# Fake, never-dereferenced "device" addresses: validation must fail first.
+A16 = 0x10000          # 16-byte aligned
+MIS = 0x10002          # misaligned
+
+
+def test_rmsnorm_validation(L):
+    f = L.bi_rmsnorm
+    assert f(A16, 4096, A16, A16, 4096, None, 0, 4096, 1e-6, None) == 0       # M == 0 no-op
+    assert f(None, 4096, A16, A16, 4096, None, 4, 4096, 1e-6, None) == 1      # null x
+    assert f(A16, 4000, A16, A16, 4096, None, 4, 4096, 1e-6, None) == 1      # ldx < H
+    assert f(MIS, 4096, A16, A16, 4096, None, 4, 4096, 1e-6, None) == 1      # misaligned
+    assert f(A16, 4096, A16, A16, 4096, None, -1, 4096, 1e-6, None) == 1     # negative M
+    assert f(A16, 4096, A16, A16, 4096, None, 4, 4096, -1.0, None) == 1      # eps < 0
+    assert f(A16, 4104, A16, A16, 4104, None, 4, 4100, 1e-6, None) == 2      # H % 8
+    assert f(A16, 32768, A16, A16, 32768, None, 4, 32768, 1e-6, None) == 2   # H too large
+
+
+def test_matmul_validation(L):
+    f = L.bi_matmul
+    assert f(A16, 4096, A16, 4096, A16, 4096, 0, 0, 4096, 4096, None) == 0    # M == 0
+    assert f(None, 4096, A16, 4096, A16, 4096, 0, 8, 4096, 4096, None) == 1
+    assert f(A16, 4096, A16, 4096, A16, 4096, 7, 8, 4096, 4096, None) == 1    # bad dtype
+    assert f(A16, 4096, A16, 4000, A16, 4096, 0, 8, 4096, 4096, None) == 1    # ldw < K
+    assert f(A16, 4096, A16, 4096, MIS, 4096, 1, 8, 4096, 4096, None) == 1    # fp32 c misaligned
+    assert f(A16, 4128, A16, 4128, A16, 4096, 0, 8, 4096, 4100, None) == 2    # K % 64
+    assert f(A16, 4096, A16, 4096, A16, 4098, 0, 8, 4098, 4096, None) == 1    # ldc % 4
+    assert f(A16, 4096, A16, 4096, A16, 4096, 0, 8, 4094, 4096, None) == 2    # N % 4
+
+
+def test_kv_append_validation(L):
+    f = L.bi_kv_append
+    assert f(A16, A16, 1024, A16, 0, A16, A16, 10, 8, 128, None) == 0
+    assert f(A16, A16, 1000, A16, 3, A16, A16, 10, 8, 128, None) == 1      # ld < Hkv*D
+    assert f(A16, A16, 1024, A16, 3, A16, A16, 10, 8, 64, None) == 2       # D != 128
+    assert f(None, A16, 1024, A16, 3, A16, A16, 10, 8, 128, None) == 1
+
+
+def test_attention_validation(L):
+    ws = L.bi_attention_workspace_bytes(4, 32, 128, 1000)
+    assert ws == 4 * 32 * 4 * 130 * 4
+    dec = L.bi_attention_decode
+    args = [A16, 4096, A16, A16, 100, A16, 64, A16, A16, 4096, 4, 32, 8, 128, 1000, 0.088, A16, ws, None]
+    bad = list(args); bad[17] = ws - 4
+    assert dec(*bad) == 3                                     # workspace too small
+    bad = list(args); bad[12] = 6
+    assert dec(*bad) == 1                                     # Hq % Hkv
+    bad = list(args); bad[13] = 64
+    assert dec(*bad) == 2                                     # D != 128
+    bad = list(args); bad[14] = 64 * 16 + 1
+    assert dec(*bad) == 1                                     # max_kv_len > capacity
+    bad = list(args); bad[10] = 0
+    assert dec(*bad) == 0                                     # S == 0
+    pre = L.bi_attention_prefill
+    pargs = [A16, 4096, A16, A16, A16, A16, 100, A16, 64, A16, 4096, 2, 300, 32, 8, 128, 200, 0.088, None]
+    bad = list(pargs); bad[14] = 3
+    assert pre(*bad) == 1                                     # Hq % Hkv
+    bad = list(pargs); bad[13] = 24; bad[14] = 8
+    assert pre(*bad) == 2                                     # group 3 unsupported
+    bad = list(pargs); bad[12] = 0
+    assert pre(*bad) == 0                                     # T == 0
+
+
+def test_argmax_validation(L):
+    f = L.bi_argmax
+    assert f(A16, 100, 0, 100, A16, None) == 0
+    assert f(A16, 99, 2, 100, A16, None) == 1
+    assert f(None, 100, 2, 100, A16, None) == 1

@@ -1,0 +1,225 @@
+"""GPU parity and batch-invariance tests for bi_rmsnorm, bi_matmul, bi_argmax
+and the MFMA layout probe.  Parity: against the CPU oracle on the same seeded
+bits.  Invariance: GPU against GPU, bit for bit."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from gpu_util import bf16_f64, check_bf16, dev_bf16, host_bits, log
+from invariant_bi_rmsnorm_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from invariant_bi_rmsnorm_amd import ops as o
+    o.lib()
+    return o
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ probe
+
+def test_mfma_layout_exact(ops):
+    log("probe: layout")
+    g = np.random.default_rng(100)
+    A = g.integers(-4, 5, (16, 32)).astype(np.float32)
+    B = g.integers(-4, 5, (32, 16)).astype(np.float32)
+    c = ops.bi_probe_mfma_bf16(dev_bf16(I.f32_to_bf16(A)), dev_bf16(I.f32_to_bf16(B)))
+    sync()
+    assert np.array_equal(c.cpu().numpy(), A @ B)
+
+
+def test_mfma_result_independent_of_row_and_column_position(ops):
+    log("probe: position independence")
+    g = np.random.default_rng(101)
+    a = I.normal_bf16(g, (16, 32))
+    b = I.normal_bf16(g, (32, 16))
+    c0 = ops.bi_probe_mfma_bf16(dev_bf16(a), dev_bf16(b)).cpu().numpy()
+    for t in range(8):
+        pr = g.permutation(16)
+        pc = g.permutation(16)
+        c1 = ops.bi_probe_mfma_bf16(dev_bf16(a[pr]), dev_bf16(b[:, pc])).cpu().numpy()
+        assert np.array_equal(c1.view(np.uint32), c0[pr][:, pc].view(np.uint32))
+    # a row of a placed next to different neighbours gives the same bits
+    for t in range(8):
+        a2 = I.normal_bf16(g, (16, 32))
+        a2[3] = a[3]
+        c2 = ops.bi_probe_mfma_bf16(dev_bf16(a2), dev_bf16(b)).cpu().numpy()
+        assert np.array_equal(c2[3].view(np.uint32), c0[3].view(np.uint32))
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+def test_rmsnorm_tiny_parity_and_invariance(ops, orc):
+    w, _ = I.tiny_weights()
+    row0 = None
+    for B in I.TINY_BATCHES:
+        log(f"rmsnorm tiny B={B}")
+        x = I.tiny_x(B)
+        y, r = ops.bi_rmsnorm(dev_bf16(x), dev_bf16(w), I.TINY_EPS)
+        yb, rb = host_bits(y), r.cpu().numpy()
+        y64, r64 = orc.rmsnorm_f64(x, w, I.TINY_EPS)
+        check_bf16(yb, y64, f"rmsnorm tiny B={B}")
+        assert np.max(np.abs(rb / r64 - 1.0)) <= 1e-5
+        if row0 is None:
+            row0 = (yb[0].copy(), rb[0].copy())
+        assert np.array_equal(yb[0], row0[0]) and rb[0].view(np.uint32) == row0[1].view(np.uint32)
+
+
+@pytest.mark.parametrize("H", [8, 24, 256, 2056, 4096, 16384])
+def test_rmsnorm_parity_shapes(ops, orc, H):
+    g = np.random.default_rng(H)
+    M = 37
+    x = I.normal_bf16(g, (M, H))
+    w = I.normal_bf16(g, (H,), 1.0, 0.1)
+    log(f"rmsnorm H={H}")
+    y, r = ops.bi_rmsnorm(dev_bf16(x), dev_bf16(w), 1e-6)
+    y64, r64 = orc.rmsnorm_f64(x, w, 1e-6)
+    check_bf16(host_bits(y), y64, f"rmsnorm H={H}")
+    assert np.max(np.abs(r.cpu().numpy() / r64 - 1.0)) <= 1e-5
+
+
+def test_rmsnorm_llama_parity_and_batch_invariance(ops, orc):
+    w = I.llama_norm_weight()
+    wd = dev_bf16(w)
+    ref0 = None
+    for M in (1, 2, 3, 7, 16, 63, 64, 128, 1024, 2048):
+        log(f"rmsnorm llama M={M}")
+        x = I.llama_x(M)
+        y, r = ops.bi_rmsnorm(dev_bf16(x), wd, I.LLAMA_EPS)
+        yb, rb = host_bits(y), r.cpu().numpy()
+        y64, r64 = orc.rmsnorm_f64(x, w, I.LLAMA_EPS)
+        check_bf16(yb, y64, f"rmsnorm llama M={M}")
+        assert np.max(np.abs(rb / r64 - 1.0)) <= 1e-5
+        if ref0 is None:
+            ref0 = (yb[0].copy(), rb[:1].view(np.uint32).copy())
+        assert np.array_equal(yb[0], ref0[0]) and np.array_equal(rb[:1].view(np.uint32), ref0[1])
+
+
+def test_rmsnorm_row_position_inplace_strided_and_repeat(ops):
+    g = np.random.default_rng(7)
+    M, H = 300, 4096
+    x = I.normal_bf16(g, (M, H))
+    w = I.normal_bf16(g, (H,), 1.0, 0.1)
+    wd = dev_bf16(w)
+    y0, r0 = ops.bi_rmsnorm(dev_bf16(x), wd, 1e-6)
+    y0b = host_bits(y0)
+    perm = g.permutation(M)
+    y1, _ = ops.bi_rmsnorm(dev_bf16(x[perm]), wd, 1e-6)
+    assert np.array_equal(host_bits(y1), y0b[perm])
+    # strided rows: x lives inside a wider buffer
+    big = np.zeros((M, H + 64), np.uint16)
+    big[:, 32:32 + H] = x
+    bd = dev_bf16(big)
+    y2, _ = ops.bi_rmsnorm(bd[:, 32:32 + H], wd, 1e-6)
+    assert np.array_equal(host_bits(y2), y0b)
+    # in place
+    xd = dev_bf16(x)
+    ops.bi_rmsnorm(xd, wd, 1e-6, y=xd)
+    assert np.array_equal(host_bits(xd), y0b)
+    # run to run
+    for _ in range(5):
+        y3, r3 = ops.bi_rmsnorm(dev_bf16(x), wd, 1e-6)
+        assert np.array_equal(host_bits(y3), y0b)
+        assert np.array_equal(r3.cpu().numpy().view(np.uint32), r0.cpu().numpy().view(np.uint32))
+
+
+# ------------------------------------------------------------------ matmul
+
+@pytest.mark.parametrize("M,N,K", [(1, 4, 64), (5, 132, 256), (127, 512, 64), (128, 128, 4096),
+                                   (129, 260, 320), (300, 1028, 1024)])
+def test_matmul_small_integers_bit_exact(ops, orc, M, N, K):
+    log(f"matmul int M={M} N={N} K={K}")
+    g = np.random.default_rng(M * 7 + N)
+    A = g.integers(-4, 5, (M, K)).astype(np.float32)
+    W = g.integers(-4, 5, (N, K)).astype(np.float32)
+    a, wt = I.f32_to_bf16(A), I.f32_to_bf16(W)
+    c32 = ops.bi_matmul(dev_bf16(a), dev_bf16(wt), out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(c32.astype(np.int64), A.astype(np.int64) @ W.T.astype(np.int64))
+    c16 = host_bits(ops.bi_matmul(dev_bf16(a), dev_bf16(wt)))
+    assert np.array_equal(c16, orc.matmul(a, wt, out="bf16"))   # exact value -> unique rounding
+
+
+def test_matmul_tiny_chain_parity_and_invariance(ops, orc):
+    w, wt = I.tiny_weights()
+    ref0 = None
+    for B in I.TINY_BATCHES:
+        log(f"tiny chain B={B}")
+        x = I.tiny_x(B)
+        y, _ = ops.bi_rmsnorm(dev_bf16(x), dev_bf16(w), I.TINY_EPS)
+        c = host_bits(ops.bi_matmul(y, dev_bf16(wt)))
+        y_or, _ = orc.rmsnorm(x, w, I.TINY_EPS)            # the oracle's own chain
+        check_bf16(c, orc.matmul_f64(y_or, wt), f"tiny chain B={B}")
+        if ref0 is None:
+            ref0 = c[0].copy()
+        assert np.array_equal(c[0], ref0)
+
+
+@pytest.mark.parametrize("N", list(I.LLAMA_N))
+def test_matmul_llama_parity_sampled(ops, orc, N):
+    wt = I.llama_weight(N)
+    wd = dev_bf16(wt)
+    g = np.random.default_rng(N)
+    for M in (1, 3, 64, 256, 2048):
+        log(f"matmul llama parity N={N} M={M}")
+        x = I.llama_x(M)
+        c = host_bits(ops.bi_matmul(dev_bf16(x), wd))
+        rows = np.unique(np.concatenate([[0, M - 1], g.integers(0, M, 6)]))
+        check_bf16(c[rows], orc.matmul_f64(x[rows], wt), f"matmul N={N} M={M}")
+
+
+@pytest.mark.parametrize("N", list(I.LLAMA_N))
+def test_matmul_llama_batch_invariance_sweep(ops, N):
+    """Every M of the sweep: rows of a batch of M equal the same rows computed
+    inside the largest batch, bit for bit; also under row shuffles and offsets."""
+    wd = dev_bf16(I.llama_weight(N))
+    x = I.llama_x(2048)
+    xd = dev_bf16(x)
+    full = host_bits(ops.bi_matmul(xd, wd))
+    full32 = ops.bi_matmul(xd, wd, out_dtype=torch.float32).cpu().numpy().view(np.uint32)
+    for M in I.M_SWEEP:
+        c = host_bits(ops.bi_matmul(xd[:M], wd))
+        assert np.array_equal(c, full[:M]), f"N={N} M={M}"
+    log(f"matmul sweep N={N} ok")
+    g = np.random.default_rng(3)
+    for M, off in ((1, 1000), (17, 333), (200, 1848), (129, 5)):
+        c = host_bits(ops.bi_matmul(xd[off:off + M], wd))
+        assert np.array_equal(c, full[off:off + M])
+        c32 = ops.bi_matmul(xd[off:off + M], wd, out_dtype=torch.float32).cpu().numpy().view(np.uint32)
+        assert np.array_equal(c32, full32[off:off + M])
+    perm = g.permutation(2048)
+    c = host_bits(ops.bi_matmul(dev_bf16(x[perm]), wd))
+    assert np.array_equal(c, full[perm])
+
+
+def test_matmul_repeat_bitwise(ops):
+    g = np.random.default_rng(9)
+    a = dev_bf16(I.normal_bf16(g, (333, 2048)))
+    wt = dev_bf16(I.normal_bf16(g, (1000, 2048), 0, 0.02))
+    c0 = host_bits(ops.bi_matmul(a, wt))
+    for _ in range(5):
+        assert np.array_equal(host_bits(ops.bi_matmul(a, wt)), c0)
+
+
+# ------------------------------------------------------------------ argmax
+
+def test_argmax_matches_oracle(ops, orc):
+    g = np.random.default_rng(5)
+    x = g.standard_normal((40, 32000)).astype(np.float32)
+    for r in range(0, 40, 4):
+        i, j = sorted(g.choice(32000, 2, replace=False))
+        x[r, i] = x[r, j] = x[r].max() + 1.0
+    x[13, 777] = np.nan
+    ids = ops.bi_argmax(torch.from_numpy(x).cuda()).cpu().numpy()
+    assert np.array_equal(ids, orc.argmax(x))
+    assert ids[13] == -1
