@@ -92,7 +92,7 @@ int bi_rmsnorm(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
  * a  [M][lda] bf16; wt [N][ldw] bf16 = the logical weight W[K][N] stored
  * transposed (the K-contiguous layout of a linear layer); c [M][ldc], bf16
  * (round to nearest even) or fp32 per c_dtype.
- * Requires K % 64 == 0, N % 4 == 0, lda/ldw % 8 == 0, ldc % 4 == 0,
+ * Requires K % 32 == 0, N % 4 == 0, lda/ldw % 8 == 0, ldc % 4 == 0,
  * a/wt 16-byte aligned, c 8-byte (bf16) / 16-byte (fp32) aligned.
  */
 int bi_matmul(const void* a, int64_t lda, const void* wt, int64_t ldw,
