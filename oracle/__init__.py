@@ -56,6 +56,12 @@ def _load():
     lib.or_attention.argtypes = [P, I64, P, P, P, I64, I32, I32, I32, D, P, P, P]
     lib.or_argmax.argtypes = [P, I64, I64, I64, P]
     lib.or_num_threads.restype = ctypes.c_int
+    lib.or_rope.argtypes = [P, P, P, I64, I32, I32, D]
+    lib.or_silu_mul.argtypes = [P, P, P, I64]
+    lib.or_add.argtypes = [P, P, P, I64]
+    lib.or_toy_scratch_bytes.argtypes = [P, I64]
+    lib.or_toy_scratch_bytes.restype = I64
+    lib.or_toy_forward.argtypes = [P, P, P, P, P, P, I64, P, P]
     _lib = lib
     return lib
 
@@ -194,3 +200,61 @@ def argmax(logits):
     ids = np.empty(rows, dtype=np.int32)
     _load().or_argmax(_p(x), V, rows, V, _p(ids))
     return ids
+
+
+# --------------------------------------------------------------------------
+# Toy decoder ops (page "la température zéro n'est pas déterministe",
+# introduction: greedy decoding of one prompt repeated 1000 times; the model is
+# read as a Llama-style pre-norm decoder, see oracle.c).
+# --------------------------------------------------------------------------
+
+def rope(x, pos, theta: float = 10000.0):
+    """x [T,H,D] bf16 bits, pos [T] -> rotated bf16 bits (rotate-half pairing)."""
+    x = _u16(x)
+    T, H, Dm = x.shape
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    y = np.empty_like(x)
+    _load().or_rope(_p(x), _p(y), _p(pos), T, H, Dm, float(theta))
+    return y
+
+
+def silu_mul(g, u):
+    g = _u16(g); u = _u16(u)
+    out = np.empty_like(g)
+    _load().or_silu_mul(_p(g), _p(u), _p(out), g.size)
+    return out
+
+
+def add(a, b):
+    a = _u16(a); b = _u16(b)
+    out = np.empty_like(a)
+    _load().or_add(_p(a), _p(b), _p(out), a.size)
+    return out
+
+
+class _ToyCfg(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("mlp", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("eps", ctypes.c_double), ("rope_theta", ctypes.c_double)]
+
+
+def toy_forward(cfg: dict, w: dict, ids):
+    """Logits (float64 [vocab]) of the last of the prompt tokens `ids` (positions
+    0..T-1), weights as produced by invariant_bi_rmsnorm_amd.inputs.toy_weights."""
+    c = _ToyCfg(cfg["layers"], cfg["hidden"], cfg["heads"], cfg["kv_heads"], cfg["head_dim"],
+                cfg["mlp"], cfg["vocab"], float(cfg["eps"]), float(cfg["rope_theta"]))
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T = ids.size
+    keep = []
+    ptrs = []
+    for lw in w["layers"]:
+        for k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd"):
+            a = _u16(lw[k]); keep.append(a); ptrs.append(a.ctypes.data)
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    nbytes = int(_load().or_toy_scratch_bytes(ctypes.byref(c), T))
+    scratch = np.empty(nbytes, dtype=np.uint8)
+    logits = np.empty(cfg["vocab"], dtype=np.float64)
+    emb = _u16(w["embed"]); fn = _u16(w["final_norm"]); lm = _u16(w["lm_head"])
+    _load().or_toy_forward(ctypes.byref(c), _p(emb), arr, _p(fn), _p(lm), _p(ids), T,
+                           _p(scratch), _p(logits))
+    return logits

@@ -28,6 +28,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #if defined(_OPENMP)
@@ -271,4 +272,132 @@ int or_num_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* ======================================================================== */
+/* Toy decoder (greedy decoding of one prompt, the experiment of the page    */
+/* "la température zéro n'est pas déterministe", introduction, and of the    */
+/* post 論文／ブログ「Defeating Nondeterminism in LLM Inference」の技術的なポイント, */
+/* section 実装上の工夫：ツールとライブラリ).  The pages name only a            */
+/* "Transformer"; the layer is read as the usual Llama-style block:          */
+/*   h += Wo . attn(rope(Wq xn), rope(Wk xn), Wv xn),  xn = rmsnorm(h)       */
+/*   h += Wd . (silu(Wg xn) * (Wu xn)),                xn = rmsnorm(h)       */
+/*   logits = Wlm . rmsnorm(h)                                               */
+/* Every op is evaluated in double and rounded to bf16 where the model       */
+/* stores a tensor (its storage format is part of its definition); logits    */
+/* stay in double.                                                           */
+/* ======================================================================== */
+
+/* Rotary embedding, rotate-half pairing: pair (x[i], x[i + D/2]) turns by    */
+/* angle pos * theta^(-2i/D).  In/out bf16 [T][H][D].                        */
+void or_rope(const uint16_t* x, uint16_t* y, const int32_t* pos, int64_t T, int32_t H,
+             int32_t D, double theta)
+{
+    int32_t half = D / 2;
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t h = 0; h < H; ++h) {
+            const uint16_t* xr = x + (t * H + h) * (int64_t)D;
+            uint16_t* yr = y + (t * H + h) * (int64_t)D;
+            for (int32_t i = 0; i < half; ++i) {
+                double ang = (double)pos[t] * pow(theta, -2.0 * (double)i / (double)D);
+                double c = cos(ang), s = sin(ang);
+                double a = bf16_bits_to_double(xr[i]);
+                double b = bf16_bits_to_double(xr[i + half]);
+                yr[i] = double_to_bf16(a * c - b * s);
+                yr[i + half] = double_to_bf16(b * c + a * s);
+            }
+        }
+}
+
+/* act = silu(g) * u = g / (1 + exp(-g)) * u, bf16 in/out, n elements. */
+void or_silu_mul(const uint16_t* g, const uint16_t* u, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double gv = bf16_bits_to_double(g[i]);
+        out[i] = double_to_bf16(gv / (1.0 + exp(-gv)) * bf16_bits_to_double(u[i]));
+    }
+}
+
+/* out = a + b (bf16), n elements. */
+void or_add(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = double_to_bf16(bf16_bits_to_double(a[i]) + bf16_bits_to_double(b[i]));
+}
+
+typedef struct {
+    int32_t layers, hidden, heads, kv_heads, head_dim, mlp, vocab;
+    double eps, rope_theta;
+} or_toy_cfg;
+
+/* layer_w: 6 pointers per layer in the order attn_norm [H], wqkv [(Hq+2Hkv)D][H],
+ * wo [H][Hq D], mlp_norm [H], wgu [2F][H], wd [H][F].  Processes the T prompt
+ * tokens of one sequence at positions 0..T-1 and writes the logits of the last
+ * one.  scratch: caller-provided bytes, at least or_toy_scratch_bytes(cfg, T). */
+int64_t or_toy_scratch_bytes(const or_toy_cfg* c, int64_t T)
+{
+    int64_t H = c->hidden, D = c->head_dim;
+    int64_t qkv = (int64_t)(c->heads + 2 * c->kv_heads) * D;
+    int64_t u16 = T * (H * 4 + qkv * 2 + (int64_t)c->heads * D * 2 + 2 * (int64_t)c->mlp * 2
+                      + (int64_t)c->kv_heads * D * 4);
+    int64_t f64 = T * (qkv > 2 * (int64_t)c->mlp ? qkv : 2 * (int64_t)c->mlp) + T * (int64_t)c->heads * T;
+    return u16 * 2 + f64 * 8 + 4096;
+}
+
+void or_toy_forward(const or_toy_cfg* c, const uint16_t* embed, const uint16_t* const* layer_w,
+                    const uint16_t* final_norm, const uint16_t* lm_head, const int32_t* ids,
+                    int64_t T, void* scratch, double* logits)
+{
+    const int64_t H = c->hidden, D = c->head_dim, Hq = c->heads, Hkv = c->kv_heads, F = c->mlp;
+    const int64_t QKV = (Hq + 2 * Hkv) * D;
+    char* p = (char*)scratch;
+    uint16_t* h = (uint16_t*)p;    p += T * H * 2;
+    uint16_t* xn = (uint16_t*)p;   p += T * H * 2;
+    uint16_t* tmp = (uint16_t*)p;  p += T * H * 2;
+    uint16_t* attn = (uint16_t*)p; p += T * Hq * D * 2;
+    uint16_t* qkv = (uint16_t*)p;  p += T * QKV * 2;
+    uint16_t* qr = (uint16_t*)p;   p += T * Hq * D * 2;
+    uint16_t* kk = (uint16_t*)p;   p += T * Hkv * D * 2;
+    uint16_t* kr = (uint16_t*)p;   p += T * Hkv * D * 2;
+    uint16_t* vv = (uint16_t*)p;   p += T * Hkv * D * 2;
+    uint16_t* gu = (uint16_t*)p;   p += T * 2 * F * 2;
+    uint16_t* act = (uint16_t*)p;  p += T * F * 2;
+    uint16_t* gg = (uint16_t*)p;   p += T * F * 2;
+    uint16_t* uu = (uint16_t*)p;   p += T * F * 2;
+    p = (char*)(((uintptr_t)p + 15) & ~(uintptr_t)15);
+    double* sc = (double*)p;       /* attention score scratch: T*Hq*T doubles */
+    int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)T);
+    for (int64_t t = 0; t < T; ++t) pos[t] = (int32_t)t;
+
+    for (int64_t t = 0; t < T; ++t)
+        memcpy(h + t * H, embed + (int64_t)ids[t] * H, (size_t)H * 2);
+
+    for (int32_t l = 0; l < c->layers; ++l) {
+        const uint16_t* const* w = layer_w + 6 * l;
+        or_rmsnorm(h, H, w[0], xn, H, NULL, T, H, c->eps);
+        or_matmul(xn, H, w[1], H, qkv, QKV, 0, T, QKV, H);
+        for (int64_t t = 0; t < T; ++t) {
+            memcpy(attn + t * Hq * D, qkv + t * QKV, (size_t)(Hq * D) * 2);         /* q */
+            memcpy(kk + t * Hkv * D, qkv + t * QKV + Hq * D, (size_t)(Hkv * D) * 2);
+            memcpy(vv + t * Hkv * D, qkv + t * QKV + (Hq + Hkv) * D, (size_t)(Hkv * D) * 2);
+        }
+        or_rope(attn, qr, pos, T, (int32_t)Hq, (int32_t)D, c->rope_theta);
+        or_rope(kk, kr, pos, T, (int32_t)Hkv, (int32_t)D, c->rope_theta);
+        or_attention(qr, T, pos, kr, vv, T, (int32_t)Hq, (int32_t)Hkv, (int32_t)D,
+                     1.0 / sqrt((double)D), sc, NULL, attn);
+        or_matmul(attn, Hq * D, w[2], Hq * D, tmp, H, 0, T, H, Hq * D);
+        or_add(h, tmp, h, T * H);
+        or_rmsnorm(h, H, w[3], xn, H, NULL, T, H, c->eps);
+        or_matmul(xn, H, w[4], H, gu, 2 * F, 0, T, 2 * F, H);
+        for (int64_t t = 0; t < T; ++t) {
+            memcpy(gg + t * F, gu + t * 2 * F, (size_t)F * 2);
+            memcpy(uu + t * F, gu + t * 2 * F + F, (size_t)F * 2);
+        }
+        or_silu_mul(gg, uu, act, T * F);
+        or_matmul(act, F, w[5], F, tmp, H, 0, T, H, F);
+        or_add(h, tmp, h, T * H);
+    }
+    or_rmsnorm(h + (T - 1) * H, H, final_norm, xn, H, NULL, 1, H, c->eps);
+    or_matmul_f64(xn, H, lm_head, H, logits, c->vocab, 1, c->vocab, H);
+    free(pos);
 }

@@ -23,6 +23,16 @@ MUTANTS = {
     "attention_sees_one_future_key": ("int64_t nvis = (int64_t)q_pos[t] + 1;", "int64_t nvis = (int64_t)q_pos[t] + 2;"),
     "rounding_ties_away": ("nearbyint(ldexp(x, -q))", "round(ldexp(x, -q))"),
     "argmax_ties_highest": ("x[i] > bv", "x[i] >= bv"),
+    "rope_wrong_sign": ("double_to_bf16(a * c - b * s)", "double_to_bf16(a * c + b * s)"),
+    "rope_adjacent_pairs": ("bf16_bits_to_double(xr[i + half]);", "bf16_bits_to_double(xr[(i + 1) % D]);"),
+    "rope_wrong_frequency": ("pow(theta, -2.0 * (double)i / (double)D)", "pow(theta, -1.0 * (double)i / (double)D)"),
+    "silu_wrong_sign": ("gv / (1.0 + exp(-gv))", "gv / (1.0 + exp(gv))"),
+    "add_subtracts": ("bf16_bits_to_double(a[i]) + bf16_bits_to_double(b[i])",
+                      "bf16_bits_to_double(a[i]) - bf16_bits_to_double(b[i])"),
+    "toy_no_final_norm": ("or_rmsnorm(h + (T - 1) * H, H, final_norm, xn, H, NULL, 1, H, c->eps);",
+                          "memcpy(xn, h + (T - 1) * H, (size_t)H * 2);"),
+    "toy_value_from_key_slot": ("memcpy(vv + t * Hkv * D, qkv + t * QKV + (Hq + Hkv) * D",
+                                "memcpy(vv + t * Hkv * D, qkv + t * QKV + Hq * D"),
 }
 
 
@@ -40,6 +50,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     env = dict(os.environ, BI_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_toy_pins.py"),
                         "-k", "not thread_count"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
