@@ -48,6 +48,15 @@ SIGNATURES = {
                                             _I32, _I64, _I32, _I32, _I32, _I32, _F, _P]),
     "bi_argmax": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
     "bi_probe_mfma_bf16": (ctypes.c_int, [_P, _P, _P, _P]),
+    # include/bi_toy.h
+    "bi_embed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _I64, _P]),
+    "bi_rope_table": (ctypes.c_int, [_P, _I32, _I32, ctypes.c_double, _P]),
+    "bi_rope": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I64, _P, _I32, _P]),
+    "bi_add": (ctypes.c_int, [_P, _P, _P, _I64, _P]),
+    "bi_silu_mul": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _P]),
+    "bi_gather_rows": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P]),
+    "bi_toy_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32]),
+    "bi_toy_step": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P, _P, _P]),
 }
 
 _lib = None
@@ -244,3 +253,64 @@ def bi_probe_mfma_bf16(a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.T
     c = torch.empty((16, 16), dtype=torch.float32, device=a.device)
     _check(lib().bi_probe_mfma_bf16(_ptr(a), _ptr(b), _ptr(c), _stream(stream)), "bi_probe_mfma_bf16")
     return c
+
+
+# ---------------------------------------------------------------------------
+# include/bi_toy.h element-wise ops
+# ---------------------------------------------------------------------------
+
+def bi_embed(table: torch.Tensor, ids: torch.Tensor, out: torch.Tensor = None, stream=None):
+    _need(table, torch.bfloat16, "table"); _need(ids, torch.int32, "ids")
+    V, H = table.shape
+    T = ids.shape[0]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=table.device)
+    _check(lib().bi_embed(_ptr(table), V, H, _ptr(ids), T, _ptr(out), _ld(out), _stream(stream)),
+           "bi_embed")
+    return out
+
+
+def bi_rope_table(max_pos: int, D: int, theta: float, stream=None) -> torch.Tensor:
+    t = torch.empty((max_pos * D,), dtype=torch.float32, device="cuda")
+    _check(lib().bi_rope_table(_ptr(t), max_pos, D, float(theta), _stream(stream)), "bi_rope_table")
+    return t
+
+
+def bi_rope(x: torch.Tensor, pos: torch.Tensor, table: torch.Tensor, max_pos: int, stream=None):
+    """In place on x [T, H, D] (rows may be strided)."""
+    H, D, ld = _heads_view(x, "x")
+    _need(pos, torch.int32, "pos")
+    _check(lib().bi_rope(_ptr(x), ld, H, D, _ptr(pos), x.shape[0], _ptr(table), max_pos,
+                         _stream(stream)), "bi_rope")
+    return x
+
+
+def bi_add(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor = None, stream=None):
+    _need(a, torch.bfloat16, "a"); _need(b, torch.bfloat16, "b")
+    if out is None:
+        out = torch.empty_like(a)
+    _check(lib().bi_add(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)), "bi_add")
+    return out
+
+
+def bi_silu_mul(gu: torch.Tensor, out: torch.Tensor = None, stream=None):
+    """gu [T, 2F] (gate | up) -> out [T, F]."""
+    _need(gu, torch.bfloat16, "gu")
+    T, F2 = gu.shape
+    F = F2 // 2
+    if out is None:
+        out = torch.empty((T, F), dtype=torch.bfloat16, device=gu.device)
+    _check(lib().bi_silu_mul(_ptr(gu), _ld(gu), F, _ptr(out), _ld(out), T, _stream(stream)),
+           "bi_silu_mul")
+    return out
+
+
+def bi_gather_rows(src: torch.Tensor, rows: torch.Tensor, out: torch.Tensor = None, stream=None):
+    _need(src, torch.bfloat16, "src"); _need(rows, torch.int32, "rows")
+    n, W = src.shape
+    R = rows.shape[0]
+    if out is None:
+        out = torch.empty((R, W), dtype=torch.bfloat16, device=src.device)
+    _check(lib().bi_gather_rows(_ptr(src), _ld(src), n, _ptr(rows), R, W, _ptr(out), _ld(out),
+                                _stream(stream)), "bi_gather_rows")
+    return out

@@ -1,0 +1,260 @@
+"""Toy greedy-decode engine on top of bi_toy_step (include/bi_toy.h).
+
+The experiment (page "la température zéro n'est pas déterministe",
+introduction; post 論文／ブログ「Defeating Nondeterminism in LLM Inference」の
+技術的なポイント, section 実装上の工夫：ツールとライブラリ): one prompt decoded
+greedily many times while the server's load changes from run to run; count the
+distinct completions.
+
+`ToyEngine` owns the device buffers (weights, per-layer paged KV caches, the
+rotary table, the workspace) and a host-side block allocator; `step()` packs
+one mixed batch (decode tokens first, then prefill chunks) into a
+bi_toy_step_desc and runs the C driver.  `run_load_experiment()` is the
+continuous-batching load generator: target requests (the fixed prompt) and
+random other requests arrive and leave at random, prefill is chunked at random
+sizes, and the batch order is shuffled every step.  All arithmetic runs in
+libbi.so; this module only schedules and marshals.
+"""
+from __future__ import annotations
+
+import ctypes
+import hashlib
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import ops
+from .inputs import BLOCK
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("mlp", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("max_pos", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("layer", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int64), ("rope_table", ctypes.c_void_p)]
+
+
+class _Step(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("S", ctypes.c_int32), ("n_decode", ctypes.c_int32),
+                ("max_q_len", ctypes.c_int32), ("max_kv_len", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32),
+                ("ids", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("slots", ctypes.c_void_p),
+                ("q_start", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("logit_rows", ctypes.c_void_p)]
+
+
+def _dev16(bits: np.ndarray, device) -> torch.Tensor:
+    a = np.array(bits, dtype=np.uint16, copy=True).view(np.int16)
+    return torch.from_numpy(a).to(device).view(torch.bfloat16)
+
+
+@dataclass
+class Request:
+    rid: int
+    prompt: np.ndarray
+    max_new: int
+    target: bool = False
+    length: int = 0                       # tokens already in the cache
+    pending: list = field(default_factory=list)
+    generated: list = field(default_factory=list)
+    blocks: list = field(default_factory=list)
+
+    def __post_init__(self):
+        self.pending = [int(t) for t in self.prompt]
+
+    @property
+    def decoding(self) -> bool:
+        return self.length >= len(self.prompt)
+
+    @property
+    def done(self) -> bool:
+        return len(self.generated) >= self.max_new
+
+
+class ToyEngine:
+    def __init__(self, cfg: dict, weights: dict, num_blocks: int, max_tokens: int, max_seqs: int,
+                 max_kv_len: int, device: str = "cuda"):
+        self.cfg = cfg
+        self.device = device
+        self.max_tokens, self.max_seqs, self.max_kv_len = max_tokens, max_seqs, max_kv_len
+        self.max_blocks = -(-max_kv_len // BLOCK)
+        L, H, D = cfg["layers"], cfg["hidden"], cfg["head_dim"]
+        Hkv = cfg["kv_heads"]
+        self.c = _Cfg(L, H, cfg["heads"], Hkv, D, cfg["mlp"], cfg["vocab"], max_kv_len,
+                      float(cfg["eps"]), float(cfg["rope_theta"]))
+        self.t = {"embed": _dev16(weights["embed"], device),
+                  "final_norm": _dev16(weights["final_norm"], device),
+                  "lm_head": _dev16(weights["lm_head"], device)}
+        self.layers = []
+        ptrs = []
+        for lw in weights["layers"]:
+            d = {k: _dev16(lw[k], device) for k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd")}
+            self.layers.append(d)
+            ptrs += [d[k].data_ptr() for k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd")]
+        self._layer_ptrs = (ctypes.c_void_p * len(ptrs))(*ptrs)
+        self.kc = [torch.zeros((num_blocks, Hkv, BLOCK, D), dtype=torch.bfloat16, device=device) for _ in range(L)]
+        self.vc = [torch.zeros((num_blocks, Hkv, D, BLOCK), dtype=torch.bfloat16, device=device) for _ in range(L)]
+        self._kp = (ctypes.c_void_p * L)(*[t.data_ptr() for t in self.kc])
+        self._vp = (ctypes.c_void_p * L)(*[t.data_ptr() for t in self.vc])
+        self.rope = ops.bi_rope_table(max_kv_len, D, cfg["rope_theta"])
+        self.w = _Weights(self.t["embed"].data_ptr(), self.t["final_norm"].data_ptr(),
+                          self.t["lm_head"].data_ptr(), ctypes.cast(self._layer_ptrs, ctypes.c_void_p),
+                          ctypes.cast(self._kp, ctypes.c_void_p), ctypes.cast(self._vp, ctypes.c_void_p),
+                          num_blocks, self.rope.data_ptr())
+        nbytes = int(ops.lib().bi_toy_workspace_bytes(ctypes.byref(self.c), max_tokens, max_seqs, max_kv_len))
+        if nbytes == 0:
+            raise ValueError("unsupported toy configuration")
+        self.ws = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+        self.next_ids = torch.empty((max_seqs,), dtype=torch.int32, device=device)
+        self.logits = torch.empty((max_seqs, cfg["vocab"]), dtype=torch.float32, device=device)
+        self.free = list(range(num_blocks))[::-1]
+        self.num_blocks = num_blocks
+
+    # ---------------------------------------------------------------- blocks
+    def _ensure_blocks(self, r: Request, new_len: int):
+        need = -(-new_len // BLOCK)
+        while len(r.blocks) < need:
+            if not self.free:
+                raise RuntimeError("KV block pool exhausted")
+            r.blocks.append(self.free.pop())
+
+    def release(self, r: Request):
+        self.free.extend(r.blocks)
+        r.blocks = []
+
+    # ---------------------------------------------------------------- one step
+    def step(self, work, want_logits: bool = False):
+        """work: list of (request, n_tokens) with all decode entries (n == 1 and
+        request decoding) first.  Returns next ids (numpy [S]) and optionally
+        logits (numpy [S, vocab])."""
+        S = len(work)
+        n_decode = 0
+        while n_decode < S and work[n_decode][0].decoding and work[n_decode][1] == 1:
+            n_decode += 1
+        ids, pos, slots, q_start, kv_lens, rows = [], [], [], [0], [], []
+        table = np.zeros((S, self.max_blocks), dtype=np.int32)
+        max_q = 1
+        for s, (r, n) in enumerate(work):
+            toks = r.pending[:n]
+            new_len = r.length + n
+            if new_len > self.max_kv_len:
+                raise RuntimeError("sequence longer than max_kv_len")
+            self._ensure_blocks(r, new_len)
+            p = np.arange(r.length, new_len)
+            bl = np.asarray(r.blocks, dtype=np.int32)
+            ids += toks
+            pos.append(p)
+            slots.append(bl[p // BLOCK] * BLOCK + p % BLOCK)
+            q_start.append(q_start[-1] + n)
+            kv_lens.append(new_len)
+            rows.append(q_start[-1] - 1)
+            table[s, :len(bl)] = bl
+            max_q = max(max_q, n)
+        T = q_start[-1]
+        if T > self.max_tokens or S > self.max_seqs:
+            raise RuntimeError("step larger than the workspace")
+        dev = self.device
+        host = np.concatenate([np.asarray(ids, np.int32), np.concatenate(pos).astype(np.int32),
+                               np.concatenate(slots).astype(np.int32), np.asarray(q_start, np.int32),
+                               np.asarray(kv_lens, np.int32), np.asarray(rows, np.int32), table.ravel()])
+        buf = torch.from_numpy(host).to(dev)
+        o = 0
+        def take(n):
+            nonlocal o
+            t = buf[o:o + n]
+            o += n
+            return t
+        d_ids, d_pos, d_slots = take(T), take(T), take(T)
+        d_qs, d_kv, d_rows = take(S + 1), take(S), take(S)
+        d_tab = take(S * self.max_blocks)
+        st = _Step(T, S, n_decode, max_q, self.max_kv_len, self.max_blocks,
+                   d_ids.data_ptr(), d_pos.data_ptr(), d_slots.data_ptr(), d_qs.data_ptr(),
+                   d_kv.data_ptr(), d_tab.data_ptr(), d_rows.data_ptr())
+        stream = torch.cuda.current_stream().cuda_stream
+        rc = ops.lib().bi_toy_step(ctypes.byref(self.c), ctypes.byref(self.w), ctypes.byref(st),
+                                   self.ws.data_ptr(), self.ws.numel(), self.next_ids.data_ptr(),
+                                   self.logits.data_ptr() if want_logits else None, stream)
+        if rc != 0:
+            raise ops.BiError(rc, "bi_toy_step")
+        nxt = self.next_ids[:S].cpu().numpy()
+        lg = self.logits[:S].cpu().numpy() if want_logits else None
+        for s, (r, n) in enumerate(work):
+            r.length += n
+            del r.pending[:n]
+            if not r.pending:                 # the step consumed the last pending token
+                r.generated.append(int(nxt[s]))
+                r.pending = [int(nxt[s])]
+        return nxt, lg
+
+
+def completion_hash(tokens) -> str:
+    return hashlib.sha256(np.asarray(tokens, dtype=np.int32).tobytes()).hexdigest()[:16]
+
+
+def run_load_experiment(engine: ToyEngine, prompt: np.ndarray, n_runs: int, n_new: int, seed: int,
+                        max_active: int = 64, max_step_tokens: int = 1024, other_prompt=(1, 512),
+                        other_new=(1, 256), chunk=(16, 512), progress=None):
+    """Decode `prompt` greedily n_runs times (n_new tokens each) inside a
+    randomly varying continuous batch.  Returns (list of completion hashes,
+    stats).  Each run of the prompt is one request; it shares every step with
+    0..max_active-1 other requests (other runs of the prompt and random
+    requests), arriving and leaving at random, in shuffled order."""
+    g = np.random.default_rng(seed)
+    V = engine.cfg["vocab"]
+    active: list[Request] = []
+    results = []
+    targets_started = 0
+    rid = 0
+    cap = int(g.integers(1, max_active + 1))
+    steps = 0
+    co_load = []
+    while len(results) < n_runs:
+        if g.random() < 0.02:                  # the server's load level drifts
+            cap = 1 if g.random() < 0.25 else int(g.integers(2, max_active + 1))
+        while len(active) < cap and g.random() < 0.7:
+            if targets_started < n_runs and g.random() < 0.5:
+                active.append(Request(rid, prompt, n_new, target=True))
+                targets_started += 1
+            else:
+                lp = int(g.integers(other_prompt[0], other_prompt[1] + 1))
+                active.append(Request(rid, g.integers(0, V, lp).astype(np.int32),
+                                      int(g.integers(other_new[0], other_new[1] + 1))))
+            rid += 1
+        if not any(r.target for r in active) and targets_started < n_runs and len(active) < max_active:
+            active.append(Request(rid, prompt, n_new, target=True))
+            targets_started += 1
+            rid += 1
+        dec = [r for r in active if r.decoding]
+        pre = [r for r in active if not r.decoding]
+        g.shuffle(dec)
+        g.shuffle(pre)
+        work = [(r, 1) for r in dec]
+        budget = max_step_tokens - len(work)
+        for r in pre:
+            if budget <= 0:
+                break
+            n = min(len(r.pending), int(g.integers(chunk[0], chunk[1] + 1)), budget)
+            work.append((r, n))
+            budget -= n
+        engine.step(work)
+        steps += 1
+        co_load.append(len(work) - 1)
+        for r in list(active):
+            if r.done:
+                if r.target:
+                    results.append(completion_hash(r.generated[:n_new]))
+                engine.release(r)
+                active.remove(r)
+        if progress and steps % 500 == 0:
+            progress(f"steps={steps} finished_runs={len(results)} active={len(active)} cap={cap}")
+    for r in active:
+        engine.release(r)
+    return results, {"steps": steps, "co_load_min": int(min(co_load)), "co_load_max": int(max(co_load)),
+                     "co_load_mean": float(np.mean(co_load))}

@@ -1,0 +1,32 @@
+"""The end-to-end bar for the toy decoder's logits is derived, not guessed:
+an independent fp32 evaluation (numpy) of the same bf16 model, compared with
+the fp64 oracle, shows how far two correct evaluations drift apart once their
+~100 bf16 roundings per forward differ.  The GPU bar (error RMS <= 2e-2 and
+max error <= 1e-1 of the logits' RMS) must admit that evaluation.  No GPU."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from invariant_bi_rmsnorm_amd import inputs as I
+from toy_ref32 import toy_logits_fp32
+
+TOY_RMS_BAR = 2e-2
+TOY_MAX_BAR = 1e-1
+
+
+def test_two_correct_evaluations_fit_the_toy_bar(orc):
+    w = I.toy_weights(I.TOY)
+    ids = I.toy_prompt(I.TOY, 64)
+    ref = orc.toy_forward(I.TOY, w, ids)
+    alt = toy_logits_fp32(I.TOY, w, ids)
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    err = np.abs(alt - ref)
+    rms_err = math.sqrt(float(np.mean(err ** 2)))
+    print(f"fp32 vs fp64: rms err / rms = {rms_err / rms:.3e}, max err / rms = {err.max() / rms:.3e}")
+    assert rms_err <= TOY_RMS_BAR * rms
+    assert err.max() <= TOY_MAX_BAR * rms
+    # the spread is real (not zero): a 1e-2-of-RMS bar on the end-to-end
+    # logits would reject a correct implementation
+    assert rms_err > 5e-3 * rms

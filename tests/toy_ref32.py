@@ -1,0 +1,70 @@
+"""An independent fp32 evaluation of the toy decoder forward (numpy), used only
+to measure how far two correct evaluations of the bf16 model drift apart when
+they round differently.  That spread sets the end-to-end bar for the GPU's
+toy logits; each op is held to the per-op bar separately."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from invariant_bi_rmsnorm_amd import inputs as I
+
+
+def _f(b):
+    return I.bf16_to_f32(b)
+
+
+def _r16(x):
+    return I.f32_to_bf16(np.asarray(x, np.float32))
+
+
+def toy_logits_fp32(cfg: dict, w: dict, ids) -> np.ndarray:
+    T = len(ids)
+    H, D, Hq, Hkv, F = cfg["hidden"], cfg["head_dim"], cfg["heads"], cfg["kv_heads"], cfg["mlp"]
+    G = Hq // Hkv
+    eps = np.float32(cfg["eps"])
+
+    def rms(x, wt):
+        xf = _f(x).astype(np.float32)
+        r = 1 / np.sqrt((xf * xf).mean(-1, keepdims=True) + eps)
+        return _r16(xf * r * _f(wt))
+
+    def mm(a, wt):
+        return _r16(_f(a).astype(np.float32) @ _f(wt).astype(np.float32).T)
+
+    def rope(x, pos):
+        half = D // 2
+        i = np.arange(half)
+        ang = pos[:, None].astype(np.float64) * cfg["rope_theta"] ** (-2.0 * i / D)
+        c = np.cos(ang).astype(np.float32)[:, None, :]
+        s = np.sin(ang).astype(np.float32)[:, None, :]
+        xf = _f(x)
+        a, b = xf[..., :half], xf[..., half:]
+        return _r16(np.concatenate([a * c - b * s, b * c + a * s], -1))
+
+    pos = np.arange(T)
+    h = w["embed"][np.asarray(ids)]
+    causal = np.tril(np.ones((T, T), bool))
+    for lw in w["layers"]:
+        xn = rms(h, lw["attn_norm"])
+        qkv = mm(xn, lw["wqkv"]).reshape(T, Hq + 2 * Hkv, D)
+        q = rope(qkv[:, :Hq], pos)
+        k = rope(qkv[:, Hq:Hq + Hkv], pos)
+        v = qkv[:, Hq + Hkv:]
+        out = np.zeros((T, Hq, D), np.float32)
+        for hh in range(Hq):
+            s = (_f(q[:, hh]) @ _f(k[:, hh // G]).T) / np.float32(math.sqrt(D))
+            s = np.where(causal, s, -np.inf)
+            p = np.exp(s - s.max(-1, keepdims=True))
+            p /= p.sum(-1, keepdims=True)
+            out[:, hh] = p @ _f(v[:, hh // G])
+        o = mm(_r16(out).reshape(T, -1), lw["wo"])
+        h = _r16(_f(h) + _f(o))
+        xn = rms(h, lw["mlp_norm"])
+        gu = _f(mm(xn, lw["wgu"]))
+        g, u = gu[:, :F], gu[:, F:]
+        d = mm(_r16(g / (1 + np.exp(-g)) * u), lw["wd"])
+        h = _r16(_f(h) + _f(d))
+    xn = rms(h[-1:], w["final_norm"])
+    return (_f(xn) @ _f(w["lm_head"]).astype(np.float32).T)[0].astype(np.float64)
