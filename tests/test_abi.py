@@ -11,13 +11,17 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "bi.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 def declared_symbols():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bi_[a-z0-9_]+)\s*\(", text)))
+    syms = set()
+    for name in sorted(os.listdir(INCLUDE)):
+        if name.endswith(".h"):
+            text = open(os.path.join(INCLUDE, name)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            syms |= set(re.findall(r"\b(bi_[a-z0-9_]+)\s*\(", text))
+    return sorted(syms)
 
 
 @pytest.fixture(scope="module")
@@ -145,3 +149,17 @@ def test_argmax_validation(L):
     assert f(A16, 100, 0, 100, A16, None) == 0
     assert f(A16, 99, 2, 100, A16, None) == 1
     assert f(None, 100, 2, 100, A16, None) == 1
+
+
+def test_toy_entry_validation(L):
+    assert L.bi_embed(A16, 10, 64, A16, 0, A16, 64, None) == 0
+    assert L.bi_embed(None, 10, 64, A16, 3, A16, 64, None) == 1
+    assert L.bi_embed(A16, 10, 60, A16, 3, A16, 64, None) == 2            # H % 8
+    assert L.bi_add(A16, A16, A16, 12, None) == 2                          # n % 8
+    assert L.bi_add(A16, None, A16, 16, None) == 1
+    assert L.bi_silu_mul(A16, 100, 64, A16, 64, 2, None) == 1              # ldgu < 2F
+    assert L.bi_rope(A16, 100, 1, 128, A16, 2, A16, 10, None) == 1         # ldx < H*D
+    assert L.bi_rope_table(None, 10, 128, 10000.0, None) == 1
+    assert L.bi_gather_rows(A16, 64, 5, A16, 2, 64, A16, 60, None) == 1    # ldd < W
+    assert L.bi_toy_workspace_bytes(None, 10, 2, 100) == 0
+    assert L.bi_toy_step(None, None, None, None, 0, None, None, None) == 1
