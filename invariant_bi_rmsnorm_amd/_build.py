@@ -11,8 +11,14 @@ from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+BASELINE = os.path.join(CSRC, "baseline")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbi.so")
+# The non-invariant baseline library: the same ABI, with the batch-dependent
+# strategies of csrc/baseline/ in place of the invariant GEMM, RMSNorm and
+# decode.  Used only for measurement and to show the invariance tests can fail.
+LIB_NB = os.path.join(HERE, "libbi_nb.so")
+REPLACED_IN_NB = {"gemm.hip", "rmsnorm.hip", "attn_decode.hip"}
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,6 +37,10 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+def baseline_sources():
+    return sorted(os.path.join(BASELINE, f) for f in os.listdir(BASELINE) if f.endswith(".hip"))
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
     cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
@@ -40,16 +50,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, sources()))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+def _link(objs, out):
+    tmp = out + ".tmp"
+    # -Bsymbolic: calls between entry points bind inside their own library, so
+    # both libraries can be loaded into one process
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-Bsymbolic", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(jobs: int = 8) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    nb_srcs = baseline_sources()
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = dict(zip(srcs + nb_srcs, ex.map(_compile, srcs + nb_srcs)))
+    _link([objs[s] for s in srcs], LIB)
+    _link([objs[s] for s in srcs if os.path.basename(s) not in REPLACED_IN_NB] +
+          [objs[s] for s in nb_srcs], LIB_NB)
     return LIB
 
 

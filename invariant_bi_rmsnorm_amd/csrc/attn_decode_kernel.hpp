@@ -1,0 +1,292 @@
+// attn_decode_kernel.hpp -- the paged decode kernels (see attn_decode.hip for
+// the design).  Splits are `split_len` tokens; the library's bi_attention_decode
+// always uses 256 (fixed-size splits), the non-invariant baseline derives the
+// length from the batch.
+#pragma once
+#include "attn_core.hpp"
+
+using namespace bi_attn;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxSeqs = 4096;
+constexpr int kPtStride = kSplit + 8;   // bf16 per row of the P^T buffer (16 B pad)
+
+__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+
+// zero elements j >= nvalid of an 8 x bf16 vector (nvalid in 0..8)
+__device__ __forceinline__ u32x4 keep_first(u32x4 v, int nvalid)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int j = 2 * e;
+        uint32_t w = v[e];
+        if (j >= nvalid) w &= 0xffff0000u;
+        if (j + 1 >= nvalid) w &= 0x0000ffffu;
+        v[e] = w;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+    const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, int64_t num_blocks, const int32_t* __restrict__ bt,
+    int max_blocks, const int32_t* __restrict__ kv_lens, int S, int Hq, int Hkv,
+    int max_splits, int split_len, float scale_log2, float* __restrict__ ws)
+{
+    __shared__ int s_off[kMaxSeqs + 1];
+    __shared__ int s_part[kThreads];
+    __shared__ float s_max[4][16];
+    __shared__ __attribute__((aligned(16))) uint16_t s_pt[16 * kPtStride];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const int g = blockIdx.y;
+    const int G = Hq / Hkv;
+    const int cap = min(max_blocks * kBlock, max_splits * split_len);
+
+    // ---- exclusive prefix of split counts (integers: any order gives the same)
+    const int per = (S + kThreads - 1) / kThreads;
+    const int b0 = tid * per;
+    int local = 0;
+    for (int j = 0; j < per; ++j) {
+        const int s = b0 + j;
+        if (s < S) local += (clamp_len(kv_lens[s], cap) + split_len - 1) / split_len;
+    }
+    s_part[tid] = local;
+    __syncthreads();
+    for (int o = 1; o < kThreads; o <<= 1) {
+        const int v = (tid >= o) ? s_part[tid - o] : 0;
+        __syncthreads();
+        s_part[tid] += v;
+        __syncthreads();
+    }
+    int run = s_part[tid] - local;
+    for (int j = 0; j < per; ++j) {
+        const int s = b0 + j;
+        if (s < S) {
+            s_off[s] = run;
+            run += (clamp_len(kv_lens[s], cap) + split_len - 1) / split_len;
+        }
+    }
+    if (tid == kThreads - 1) s_off[S] = s_part[kThreads - 1];
+    __syncthreads();
+    const int total = s_off[S];
+
+    for (int w = blockIdx.x; w < total; w += gridDim.x) {
+        // sequence of item w: the largest s with s_off[s] <= w
+        int lo = 0, hi = S - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= w) lo = mid; else hi = mid - 1;
+        }
+        const int s = lo;
+        const int i = w - s_off[s];
+        const int Lseq = clamp_len(kv_lens[s], cap);
+        const int t0 = i * split_len;
+        // tokens of this split: [t0, L); with split_len == 256 (the library's
+        // only value) L is the sequence length
+        const int L = min(Lseq, t0 + split_len);
+        const int32_t* btr = bt + (int64_t)s * max_blocks;
+
+        // values operands of this wave's two head-dim tiles, all 8 chunks
+        // (issued first: they do not depend on the scores)
+        u32x4 vv[kChunks][2];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int tok = t0 + 32 * c + 8 * grp;
+            int blk = -1;
+            if (tok < L) blk = btr[tok >> 4];
+            const bool ok = tok < L && blk >= 0 && blk < num_blocks;
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd) {
+                const int d = 16 * (2 * wave + dd) + col;
+                vv[c][dd] = zero_u32x4();
+                if (ok) {
+                    vv[c][dd] = ld16(vc + (((int64_t)blk * Hkv + g) * kD + d) * kBlock + (tok & 15));
+                    if (tok + 8 > L) vv[c][dd] = keep_first(vv[c][dd], L - tok);
+                }
+            }
+        }
+
+        // query operands: column col is query head g*G + col
+        bf16x8 qf[4];
+        const bool qok = col < G;
+        const uint16_t* qrow = q + (int64_t)s * ldq + (int64_t)(g * G + col) * kD + 8 * grp;
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc) qf[dc] = as_bf16x8(qok ? ld16(qrow + 32 * dc) : zero_u32x4());
+
+        // scores of chunks 2*wave, 2*wave+1
+        float sv[2][8];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const int c = 2 * wave + cc;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int tok = t0 + 32 * c + score_row_token(col, h);
+                bf16x8 kf[4];
+                int blk = -1;
+                if (tok < L) blk = btr[tok >> 4];
+                const bool ok = tok < L && blk >= 0 && blk < num_blocks;
+                const uint16_t* kp = kc + (((int64_t)blk * Hkv + g) * kBlock + (tok & 15)) * kD + 8 * grp;
+#pragma unroll
+                for (int dc = 0; dc < 4; ++dc) kf[dc] = as_bf16x8(ok ? ld16(kp + 32 * dc) : zero_u32x4());
+                const f32x4 acc = score_tile(kf, qf);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 4 * h + r;
+                    const bool valid = (t0 + 32 * c + 8 * grp + j) < L;
+                    sv[cc][j] = valid ? scaled_score(acc[r], scale_log2) : -INFINITY;
+                }
+            }
+        }
+
+        // split max across the four waves
+        float mx = -INFINITY;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mx = fmaxf(mx, sv[cc][j]);
+        mx = colmax_finish(mx);
+        if (grp == 0) s_max[wave][col] = mx;
+        __syncthreads();
+        const float m = fmaxf(fmaxf(s_max[0][col], s_max[1][col]), fmaxf(s_max[2][col], s_max[3][col]));
+
+        // bf16 weights -> LDS as P^T[q][token]
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const int c = 2 * wave + cc;
+            uint32_t wv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                wv[j] = weight_bf16(sv[cc][j], m, (t0 + 32 * c + 8 * grp + j) < L);
+            st16(&s_pt[col * kPtStride + 32 * c + 8 * grp], as_u32x4(pack_weights(wv)));
+        }
+        __syncthreads();
+
+        // values chain over the whole split for head-dim tiles 2*wave, 2*wave+1
+        f32x4 o[2];
+        o[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        o[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float ls = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const bf16x8 pf = as_bf16x8(ld16(&s_pt[col * kPtStride + 32 * c + 8 * grp]));
+            ls = lsum_add(ls, pf);
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd) o[dd] = pv_step(as_bf16x8(vv[c][dd]), pf, o[dd]);
+        }
+        ls = lsum_finish(ls);
+
+        if (col < G) {
+            const int h = g * G + col;
+            float* base = ws + (((int64_t)s * Hq + h) * max_splits + i) * (kD + 2);
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) base[2 + 16 * (2 * wave + dd) + 4 * grp + r] = o[dd][r];
+            if (wave == 0 && grp == 0) {
+                base[0] = m;
+                base[1] = ls;
+            }
+        }
+        __syncthreads();   // s_max / s_pt are reused by the next item
+    }
+}
+
+__global__ __launch_bounds__(kD) void decode_combine_kernel(
+    const float* __restrict__ ws, const int32_t* __restrict__ kv_lens, int cap, int Hq,
+    int max_splits, int split_len, uint16_t* __restrict__ out, int64_t ldo)
+{
+    const int s = blockIdx.y;
+    const int h = blockIdx.x;
+    const int d = threadIdx.x;
+    const int L = clamp_len(kv_lens[s], cap);
+    const int n = (L + split_len - 1) / split_len;
+    uint16_t* o = out + (int64_t)s * ldo + (int64_t)h * kD + d;
+    if (n == 0) {
+        *o = 0;
+        return;
+    }
+    const float* base = ws + ((int64_t)s * Hq + h) * max_splits * (kD + 2);
+    float M = base[0];
+    float Lam = base[1];
+    float O = base[2 + d];
+    for (int i = 1; i < n; ++i) {
+        const float* p = base + (int64_t)i * (kD + 2);
+        float a, b;
+        fold_scalars(M, Lam, p[0], p[1], a, b);
+        O = fold_value(O, p[2 + d], a, b);
+    }
+    *o = (uint16_t)f32_to_bf16_rne(finish_value(O, Lam));
+}
+
+static inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workspace of split partials when splits are `split_len` tokens long.
+static inline size_t decode_ws_bytes(int32_t S, int32_t Hq, int32_t D, int32_t max_kv_len, int split_len)
+{
+    if (S <= 0 || Hq <= 0 || D <= 0 || max_kv_len <= 0) return 0;
+    return (size_t)S * (size_t)Hq * (size_t)ceil_div64(max_kv_len, split_len) * (size_t)(D + 2) *
+           sizeof(float);
+}
+
+// Host validation shared by every bi_attention_decode build: BI_OK to go on,
+// -1 for the S == 0 no-op, else the status to return.
+static inline int decode_validate(const void* q, int64_t ldq, const void* k_cache, const void* v_cache,
+                                  int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* kv_lens, const void* out, int64_t ldo, int32_t S,
+                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t max_kv_len, float scale,
+                                  const void* ws)
+{
+    if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_blocks <= 0 || num_blocks <= 0)
+        return BI_ERR_INVALID_ARGUMENT;
+    if (max_kv_len <= 0 || (int64_t)max_kv_len > (int64_t)max_blocks * kBlock)
+        return BI_ERR_INVALID_ARGUMENT;
+    if (Hq % Hkv) return BI_ERR_INVALID_ARGUMENT;
+    if (!(scale == scale)) return BI_ERR_INVALID_ARGUMENT;
+    if (S > 0 && (!q || !k_cache || !v_cache || !block_table || !kv_lens || !out || !ws))
+        return BI_ERR_INVALID_ARGUMENT;
+    if (ldq < (int64_t)Hq * D || ldo < (int64_t)Hq * D || (ldq % 8) || (ldo % 8))
+        return BI_ERR_INVALID_ARGUMENT;
+    if (S > 0 && (!bi_aligned(q, 16) || !bi_aligned(k_cache, 16) || !bi_aligned(v_cache, 16) ||
+                  !bi_aligned(out, 2) || !bi_aligned(ws, 16) || !bi_aligned(block_table, 4) ||
+                  !bi_aligned(kv_lens, 4)))
+        return BI_ERR_INVALID_ARGUMENT;
+    if (D != kD || Hq / Hkv > 16 || S > kMaxSeqs || max_kv_len > (1 << 20) || Hkv > 65535)
+        return BI_ERR_UNSUPPORTED;
+    if (S == 0) return -1;
+    return BI_OK;
+}
+
+// Launch split + combine with splits of split_len tokens (a multiple of 32,
+// at most 256).  The invariant library always passes 256.
+static inline int decode_launch(const void* q, int64_t ldq, const void* k_cache, const void* v_cache,
+                                int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* kv_lens, void* out, int64_t ldo, int32_t S, int32_t Hq,
+                                int32_t Hkv, int32_t max_kv_len, float scale, void* ws, int split_len,
+                                void* stream)
+{
+    const int max_splits = (int)ceil_div64(max_kv_len, split_len);
+    const int64_t items_bound = (int64_t)S * max_splits;
+    const int64_t per_head = std::max<int64_t>(1, 1024 / Hkv);
+    const int P = (int)std::min<int64_t>(items_bound, per_head);
+    const float scale_log2 = scale_log2_of(scale);
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(decode_split_kernel, dim3(P, Hkv), dim3(kThreads), 0, st,
+                       (const uint16_t*)q, ldq, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
+                       num_blocks, block_table, max_blocks, kv_lens, S, Hq, Hkv, max_splits, split_len,
+                       scale_log2, (float*)ws);
+    int rc = bi_launch_status();
+    if (rc != BI_OK) return rc;
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(Hq, S), dim3(kD), 0, st, (const float*)ws,
+                       kv_lens, std::min(max_blocks * kBlock, max_splits * split_len), Hq, max_splits,
+                       split_len, (uint16_t*)out, ldo);
+    return bi_launch_status();
+}
+
+}  // namespace

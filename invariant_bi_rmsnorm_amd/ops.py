@@ -19,6 +19,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("BI_LIB") or os.path.join(_HERE, "libbi.so")
+# non-invariant baseline library (same ABI); see use_library()
+NB_LIB_PATH = os.path.join(_HERE, "libbi_nb.so")
 
 BI_OK = 0
 BI_ERR_INVALID_ARGUMENT = 1
@@ -83,6 +85,22 @@ def lib():
             f.argtypes = args
         _lib = L
     return _lib
+
+
+def use_library(path: str):
+    """Route the binding to another build of the same ABI (e.g. NB_LIB_PATH,
+    the non-invariant baseline); returns the previous path.  Each library is
+    loaded once and kept."""
+    global LIB_PATH, _lib
+    prev = LIB_PATH
+    if path != LIB_PATH:
+        _loaded[LIB_PATH] = _lib
+        LIB_PATH = path
+        _lib = _loaded.get(path)
+    return prev
+
+
+_loaded = {}
 
 
 def status_string(s: int) -> str:

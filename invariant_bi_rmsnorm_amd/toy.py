@@ -83,6 +83,7 @@ class ToyEngine:
                  max_kv_len: int, device: str = "cuda"):
         self.cfg = cfg
         self.device = device
+        self.L = ops.lib()          # the library current at construction serves every call
         self.max_tokens, self.max_seqs, self.max_kv_len = max_tokens, max_seqs, max_kv_len
         self.max_blocks = -(-max_kv_len // BLOCK)
         L, H, D = cfg["layers"], cfg["hidden"], cfg["head_dim"]
@@ -108,7 +109,7 @@ class ToyEngine:
                           self.t["lm_head"].data_ptr(), ctypes.cast(self._layer_ptrs, ctypes.c_void_p),
                           ctypes.cast(self._kp, ctypes.c_void_p), ctypes.cast(self._vp, ctypes.c_void_p),
                           num_blocks, self.rope.data_ptr())
-        nbytes = int(ops.lib().bi_toy_workspace_bytes(ctypes.byref(self.c), max_tokens, max_seqs, max_kv_len))
+        nbytes = int(self.L.bi_toy_workspace_bytes(ctypes.byref(self.c), max_tokens, max_seqs, max_kv_len))
         if nbytes == 0:
             raise ValueError("unsupported toy configuration")
         self.ws = torch.empty((nbytes,), dtype=torch.uint8, device=device)
@@ -178,7 +179,7 @@ class ToyEngine:
                    d_ids.data_ptr(), d_pos.data_ptr(), d_slots.data_ptr(), d_qs.data_ptr(),
                    d_kv.data_ptr(), d_tab.data_ptr(), d_rows.data_ptr())
         stream = torch.cuda.current_stream().cuda_stream
-        rc = ops.lib().bi_toy_step(ctypes.byref(self.c), ctypes.byref(self.w), ctypes.byref(st),
+        rc = self.L.bi_toy_step(ctypes.byref(self.c), ctypes.byref(self.w), ctypes.byref(st),
                                    self.ws.data_ptr(), self.ws.numel(), self.next_ids.data_ptr(),
                                    self.logits.data_ptr() if want_logits else None, stream)
         if rc != 0:
