@@ -141,7 +141,7 @@ size_t bi_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D, int32_t ma
  * [1, max_kv_len] and <= max_blocks*16.  scale multiplies q.k (1/sqrt(D) usually).
  * ws: device workspace of at least bi_attention_workspace_bytes(S, Hq, D, max_kv_len).
  * Requires D == 128, Hq % Hkv == 0, Hq/Hkv <= 16, 1 <= max_kv_len <= 1<<20,
- * S <= 8192, 16-byte aligned q/out/caches, ldq/ldo % 8 == 0.
+ * S <= 2048, 16-byte aligned q/out/caches, ldq/ldo % 8 == 0.
  */
 int bi_attention_decode(const void* q, int64_t ldq, const void* k_cache, const void* v_cache,
                         int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
@@ -189,6 +189,15 @@ int bi_argmax(const float* logits, int64_t ld, int64_t rows, int64_t V, int32_t*
  * this entry point to check that and the layout.  Device pointers.
  */
 int bi_probe_mfma_bf16(const void* a, const void* b, float* c, void* stream);
+
+/*
+ * Diagnostic: dst[0:bytes] = src[0:bytes] with a plain streaming copy kernel
+ * (16-byte accesses, grid-stride).  It measures the achievable HBM bandwidth
+ * that the kernels' rooflines are compared with, and is the known-size
+ * reference for scaling the memory-traffic counters.  bytes % 16 == 0,
+ * 16-byte aligned device pointers, no overlap.
+ */
+int bi_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

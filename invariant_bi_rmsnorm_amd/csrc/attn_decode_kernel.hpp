@@ -10,7 +10,7 @@ using namespace bi_attn;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxSeqs = 4096;
+constexpr int kMaxSeqs = 2048;
 constexpr int kPtStride = kSplit + 8;   // bf16 per row of the P^T buffer (16 B pad)
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
@@ -29,6 +29,11 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nvalid)
     return v;
 }
 
+// K rows of a split are staged in LDS (256 B per token row); 16-byte chunk ch
+// of row r sits at slot ch ^ kswz(r), so the 16 rows one MFMA operand read
+// touches fall in distinct banks.
+__device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
+
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t num_blocks, const int32_t* __restrict__ bt,
@@ -38,7 +43,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     __shared__ int s_off[kMaxSeqs + 1];
     __shared__ int s_part[kThreads];
     __shared__ float s_max[4][16];
-    __shared__ __attribute__((aligned(16))) uint16_t s_pt[16 * kPtStride];
+    __shared__ int s_blk[kSplit / kBlock];
+    // K of the split [256][128] bf16; after the scores it holds P^T [16][kPtStride]
+    __shared__ __attribute__((aligned(1024))) uint16_t s_k[kSplit * kD];
+    uint16_t* const s_pt = s_k;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -93,15 +101,23 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         const int L = min(Lseq, t0 + split_len);
         const int32_t* btr = bt + (int64_t)s * max_blocks;
 
+        // physical blocks of the split's 16 cache blocks (-1: none / invalid)
+        if (tid < kSplit / kBlock) {
+            const int tok = t0 + kBlock * tid;
+            int blk = -1;
+            if (tok < L) blk = btr[tok >> 4];
+            s_blk[tid] = (blk >= 0 && blk < num_blocks) ? blk : -1;
+        }
+        __syncthreads();
+
         // values operands of this wave's two head-dim tiles, all 8 chunks
         // (issued first: they do not depend on the scores)
         u32x4 vv[kChunks][2];
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
             const int tok = t0 + 32 * c + 8 * grp;
-            int blk = -1;
-            if (tok < L) blk = btr[tok >> 4];
-            const bool ok = tok < L && blk >= 0 && blk < num_blocks;
+            const int blk = tok < L ? s_blk[(tok - t0) >> 4] : -1;
+            const bool ok = blk >= 0;
 #pragma unroll
             for (int dd = 0; dd < 2; ++dd) {
                 const int d = 16 * (2 * wave + dd) + col;
@@ -120,6 +136,23 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
         for (int dc = 0; dc < 4; ++dc) qf[dc] = as_bf16x8(qok ? ld16(qrow + 32 * dc) : zero_u32x4());
 
+        // K of the split -> LDS, one 1 KB wave load = 4 token rows of 256 B
+        // (rows past the sequence are not loaded; their scores are masked)
+#pragma unroll
+        for (int it = 0; it < kSplit / 4 / 4; ++it) {
+            const int inst = wave + 4 * it;
+            const int row = 4 * inst + (lane >> 4);
+            const int tok = t0 + row;
+            const int blk = tok < L ? s_blk[row >> 4] : -1;
+            if (blk >= 0) {
+                const int gch = (lane & 15) ^ kswz(row);         // chunk landing at slot lane&15
+                __builtin_amdgcn_global_load_lds(
+                    kc + (((int64_t)blk * Hkv + g) * kBlock + (tok & 15)) * kD + gch * 8,
+                    s_k + inst * 512, 16, 0, 0);
+            }
+        }
+        __syncthreads();      // waits for this wave's loads, then for everyone's
+
         // scores of chunks 2*wave, 2*wave+1
         float sv[2][8];
 #pragma unroll
@@ -127,14 +160,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
             const int c = 2 * wave + cc;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int tok = t0 + 32 * c + score_row_token(col, h);
+                const int row = 32 * c + score_row_token(col, h);
                 bf16x8 kf[4];
-                int blk = -1;
-                if (tok < L) blk = btr[tok >> 4];
-                const bool ok = tok < L && blk >= 0 && blk < num_blocks;
-                const uint16_t* kp = kc + (((int64_t)blk * Hkv + g) * kBlock + (tok & 15)) * kD + 8 * grp;
 #pragma unroll
-                for (int dc = 0; dc < 4; ++dc) kf[dc] = as_bf16x8(ok ? ld16(kp + 32 * dc) : zero_u32x4());
+                for (int dc = 0; dc < 4; ++dc)
+                    kf[dc] = *reinterpret_cast<const bf16x8*>(s_k + row * kD + (((4 * dc + grp) ^ kswz(row)) * 8));
                 const f32x4 acc = score_tile(kf, qf);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -198,10 +228,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     }
 }
 
+// Fold of the split partials of one (sequence, query head), 128 threads (one
+// per head dim).  Splits are taken in chunks of kFoldChunk: the threads load
+// the chunk's (m, l) into LDS, one thread runs the scalar recurrence of the
+// fold in split order and leaves each split's weights (a, b) in LDS, then every
+// thread applies them to its dim.  Same operations, same order as a plain left
+// fold -- only the loads are batched.
+constexpr int kFoldChunk = 256;
+
 __global__ __launch_bounds__(kD) void decode_combine_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ kv_lens, int cap, int Hq,
     int max_splits, int split_len, uint16_t* __restrict__ out, int64_t ldo)
 {
+    __shared__ float s_m[kFoldChunk], s_l[kFoldChunk], s_a[kFoldChunk], s_b[kFoldChunk];
+    __shared__ float s_lam;
     const int s = blockIdx.y;
     const int h = blockIdx.x;
     const int d = threadIdx.x;
@@ -213,16 +253,35 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
         return;
     }
     const float* base = ws + ((int64_t)s * Hq + h) * max_splits * (kD + 2);
-    float M = base[0];
-    float Lam = base[1];
-    float O = base[2 + d];
-    for (int i = 1; i < n; ++i) {
-        const float* p = base + (int64_t)i * (kD + 2);
-        float a, b;
-        fold_scalars(M, Lam, p[0], p[1], a, b);
-        O = fold_value(O, p[2 + d], a, b);
+    float M = 0.f, Lam = 0.f, O = 0.f;
+    for (int c0 = 0; c0 < n; c0 += kFoldChunk) {
+        const int cn = min(kFoldChunk, n - c0);
+        for (int i = d; i < cn; i += kD) {
+            s_m[i] = base[(int64_t)(c0 + i) * (kD + 2)];
+            s_l[i] = base[(int64_t)(c0 + i) * (kD + 2) + 1];
+        }
+        __syncthreads();
+        if (d == 0) {
+            int i = 0;
+            if (c0 == 0) {            // the state starts as split 0's own (m, l, o)
+                M = s_m[0];
+                Lam = s_l[0];
+                i = 1;
+            }
+            for (; i < cn; ++i) fold_scalars(M, Lam, s_m[i], s_l[i], s_a[i], s_b[i]);
+            s_lam = Lam;
+        }
+        __syncthreads();
+        int i = 0;
+        if (c0 == 0) {
+            O = base[2 + d];
+            i = 1;
+        }
+#pragma unroll 8
+        for (; i < cn; ++i) O = fold_value(O, base[(int64_t)(c0 + i) * (kD + 2) + 2 + d], s_a[i], s_b[i]);
+        __syncthreads();          // the chunk's LDS is reused by the next chunk
     }
-    *o = (uint16_t)f32_to_bf16_rne(finish_value(O, Lam));
+    *o = (uint16_t)f32_to_bf16_rne(finish_value(O, s_lam));
 }
 
 static inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -273,7 +332,19 @@ static inline int decode_launch(const void* q, int64_t ldq, const void* k_cache,
 {
     const int max_splits = (int)ceil_div64(max_kv_len, split_len);
     const int64_t items_bound = (int64_t)S * max_splits;
-    const int64_t per_head = std::max<int64_t>(1, 1024 / Hkv);
+    // persistent grid: as many workgroups as can be resident at once (a
+    // second, partial round of workgroups would run at low occupancy)
+    static const int resident = [] {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel, kThreads, 0) !=
+                hipSuccess ||
+            cus <= 0 || per_cu <= 0)
+            return 1024;
+        return cus * per_cu;
+    }();
+    const int64_t per_head = std::max<int64_t>(1, resident / Hkv);
     const int P = (int)std::min<int64_t>(items_bound, per_head);
     const float scale_log2 = scale_log2_of(scale);
     hipStream_t st = (hipStream_t)stream;

@@ -25,6 +25,23 @@ __global__ __launch_bounds__(64) void probe_kernel(const uint16_t* __restrict__ 
     for (int r = 0; r < 4; ++r) c[(4 * grp + r) * 16 + col] = acc[r];
 }
 
+// Plain streaming copy, 16 bytes per lane per access, grid-stride: the
+// reference for achievable HBM bandwidth and for scaling memory counters.
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                   int64_t n16)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        dst[i] = a;
+        dst[i + stride] = b;
+        dst[i + 2 * stride] = c;
+        dst[i + 3 * stride] = d;
+    }
+    for (; i < n16; i += stride) dst[i] = src[i];
+}
+
 }  // namespace
 
 extern "C" int bi_abi_version(void) { return BI_ABI_VERSION; }
@@ -49,6 +66,22 @@ extern "C" int bi_probe_mfma_bf16(const void* a, const void* b, float* c, void* 
     if (!bi_aligned(a, 16) || !bi_aligned(b, 2) || !bi_aligned(c, 4)) return BI_ERR_INVALID_ARGUMENT;
     hipLaunchKernelGGL(probe_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, (const uint16_t*)a,
                        (const uint16_t*)b, c);
+    return bi_launch_status();
+    BI_TRY_END
+}
+
+extern "C" int bi_probe_copy(const void* src, void* dst, int64_t bytes, void* stream)
+{
+    BI_TRY_BEGIN
+    if (bytes < 0 || (bytes % 16)) return BI_ERR_INVALID_ARGUMENT;
+    if (bytes > 0 && (!src || !dst || !bi_aligned(src, 16) || !bi_aligned(dst, 16)))
+        return BI_ERR_INVALID_ARGUMENT;
+    if (bytes == 0) return BI_OK;
+    const int64_t n16 = bytes / 16;
+    const int64_t want = (n16 + 255) / 256;
+    const unsigned grid = (unsigned)(want < 256 * 16 ? want : 256 * 16);
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src,
+                       (u32x4*)dst, n16);
     return bi_launch_status();
     BI_TRY_END
 }

@@ -50,6 +50,7 @@ SIGNATURES = {
                                             _I32, _I64, _I32, _I32, _I32, _I32, _F, _P]),
     "bi_argmax": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
     "bi_probe_mfma_bf16": (ctypes.c_int, [_P, _P, _P, _P]),
+    "bi_probe_copy": (ctypes.c_int, [_P, _P, _I64, _P]),
     # include/bi_toy.h
     "bi_embed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "bi_rope_table": (ctypes.c_int, [_P, _I32, _I32, ctypes.c_double, _P]),
@@ -265,6 +266,13 @@ def bi_argmax(logits: torch.Tensor, ids: torch.Tensor = None, stream=None) -> to
     _check(lib().bi_argmax(_ptr(logits), _ld(logits), rows, V, _ptr(ids), _stream(stream)),
            "bi_argmax")
     return ids
+
+
+def bi_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check(lib().bi_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "bi_probe_copy")
 
 
 def bi_probe_mfma_bf16(a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:

@@ -144,6 +144,12 @@ def test_attention_validation(L):
     assert pre(*bad) == 0                                     # T == 0
 
 
+def test_probe_copy_validation(L):
+    assert L.bi_probe_copy(A16, A16, 0, None) == 0
+    assert L.bi_probe_copy(A16, A16, 17, None) == 1
+    assert L.bi_probe_copy(MIS, A16, 32, None) == 1
+
+
 def test_argmax_validation(L):
     f = L.bi_argmax
     assert f(A16, 100, 0, 100, A16, None) == 0
