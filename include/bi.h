@@ -162,7 +162,8 @@ int bi_attention_decode(const void* q, int64_t ldq, const void* k_cache, const v
  * q [T][ldq] bf16 (rows ordered by q_start), out [T][ldo] bf16;
  * q_start [S+1] int32 ascending with q_start[0] == 0 and q_start[S] == T;
  * kv_lens [S] int32; max_q_len >= every T_s (host-side bound for the grid).
- * Requires D == 128, Hq % Hkv == 0, Hq/Hkv in {1,2,4,8,16}.
+ * Requires D == 128, Hq % Hkv == 0, Hq/Hkv in {1,2,4,8,16}, max_blocks <= 4096
+ * (sequences up to 65536 positions), S <= 65535, Hkv <= 65535.
  */
 int bi_attention_prefill(const void* q, int64_t ldq, const int32_t* q_start,
                          const int32_t* kv_lens, const void* k_cache, const void* v_cache,

@@ -8,25 +8,29 @@
 // 「非決定モード → 決定モード」に切り替える例, section 注意点・補足実装 (fixed chunk
 // size whatever the cache state).
 //
-// Grid: (query tiles, KV heads, sequences).  A workgroup of 4 wavefronts takes
-// 64/G query tokens x the G query heads of one KV head (G = Hq/Hkv); each
-// wavefront owns 16 of those (token, head) rows as the 16 MFMA columns.  It
-// walks the ABSOLUTE 256-token splits 0, 1, ..., up to the split holding its
-// last row, staging K then V^T of each half split (128 tokens) in LDS, and
-// evaluates every split through attn_core.hpp exactly as the decode kernel does,
-// folding in registers.  Because splits are aligned to absolute position 0 and
-// the arithmetic per split does not depend on which or how many other rows
-// share the call, a row's output is the same whether its prompt arrived in one
-// piece or in chunks, and equals decode at the same length.
+// Grid: (query tiles, KV heads, sequences).  A workgroup of 8 wavefronts takes
+// 128/G query tokens x the G query heads of one KV head (G = Hq/Hkv); each
+// wavefront owns 16 of those (token, head) rows as the 16 MFMA columns.  The
+// workgroup reads its sequence's block ids into LDS once, then walks the
+// ABSOLUTE 256-token splits 0, 1, ..., up to the split holding its last row.
+// K and V^T of a split are staged in LDS with direct global-to-LDS loads,
+// double-buffered against the math: V of split i streams in while the scores
+// of split i are formed, K of split i+1 while its values are accumulated.
+// Every split is evaluated through attn_core.hpp exactly as the decode kernel
+// does, folding in registers.  Because splits are aligned to absolute position
+// 0 and the arithmetic per split does not depend on which or how many other
+// rows share the call, a row's output is the same whether its prompt arrived
+// in one piece or in chunks, and equals decode at the same length.
 #include "attn_core.hpp"
 
 using namespace bi_attn;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kHalf = kSplit / 2;        // tokens staged at once
-constexpr int kStride = kD + 8;          // bf16 per LDS row (both K and V^T stages)
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 16 * kWaves;          // (token, head) rows per workgroup
+constexpr int kMaxBlocks = 4096;            // block-table width supported (65536 positions)
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
@@ -43,6 +47,14 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nvalid)
     return v;
 }
 
+// LDS layouts of one split.  K: [256 token rows][128 dims], 16-byte chunk ch of
+// row r at slot ch ^ kswz(r) (the 16 rows of one MFMA operand read hit
+// distinct banks).  V^T: as in the cache, [16 blocks][128 dims][16 tokens], the
+// two 16-byte halves of dim row d swapped when (d >> 3) is odd (dims d and
+// d + 8 of one operand read hit distinct banks).
+__device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
+__device__ __forceinline__ int vhalf(int d, int half) { return half ^ ((d >> 3) & 1); }
+
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const int32_t* __restrict__ q_start,
     const int32_t* __restrict__ kv_lens, const uint16_t* __restrict__ kc,
@@ -50,18 +62,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     int max_blocks, uint16_t* __restrict__ out, int64_t ldo, int64_t T, int Hq, int Hkv,
     float scale_log2)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t s_buf[kHalf * kStride];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_k[kSplit * kD];     // 64 KB
+    __shared__ __attribute__((aligned(1024))) uint16_t s_v[kSplit * kD];     // 64 KB
+    __shared__ int s_bt[kMaxBlocks];         // physical block of every cache block the workgroup reads
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;
     const int grp = lane >> 4;
     const int s = blockIdx.z;
     const int g = blockIdx.y;
     const int G = Hq / Hkv;
     const int tpw = 16 / G;                 // tokens per wavefront
-    const int QT = 4 * tpw;                 // tokens per workgroup
+    const int QT = kWaves * tpw;            // tokens per workgroup
     const int qt = gridDim.x - 1 - blockIdx.x;   // longest rows first
 
     const int qs = q_start[s];
@@ -84,50 +98,71 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) qf[dc] = as_bf16x8(cvalid ? ld16(qrow + 32 * dc) : zero_u32x4());
 
+    // block ids of every cache block this workgroup reads, once (-1: none / invalid)
+    const int nblk_used = min((L + kBlock - 1) / kBlock, nsplit * (kSplit / kBlock));
+    for (int b = tid; b < nblk_used; b += kThreads) {
+        const int blk = btr[b];
+        s_bt[b] = (blk >= 0 && blk < num_blocks) ? blk : -1;
+    }
+    auto issue_k = [&](int i) {                       // K rows of split i -> s_k
+#pragma unroll
+        for (int it = 0; it < kSplit / 4 / kWaves; ++it) {
+            const int inst = wave + kWaves * it;
+            const int row = 4 * inst + (lane >> 4);
+            const int tok = i * kSplit + row;
+            const int blk = tok < L ? s_bt[tok >> 4] : -1;
+            if (blk >= 0) {
+                const int gch = (lane & 15) ^ kswz(row);
+                __builtin_amdgcn_global_load_lds(
+                    kc + (((int64_t)blk * Hkv + g) * kBlock + (tok & 15)) * kD + gch * 8,
+                    s_k + inst * 512, 16, 0, 0);
+            }
+        }
+    };
+    auto issue_v = [&](int i) {                       // V^T blocks of split i -> s_v
+#pragma unroll
+        for (int it = 0; it < kSplit / 4 / kWaves; ++it) {
+            const int inst = wave + kWaves * it;      // block inst/4, dims 32*(inst%4) ...
+            const int b = inst >> 2;
+            const int d = 32 * (inst & 3) + (lane >> 1);
+            const int tb = i * (kSplit / kBlock) + b;
+            const int blk = tb * kBlock < L ? s_bt[tb] : -1;
+            if (blk >= 0)
+                __builtin_amdgcn_global_load_lds(
+                    vc + (((int64_t)blk * Hkv + g) * kD + d) * kBlock + vhalf(d, lane & 1) * 8,
+                    s_v + inst * 512, 16, 0, 0);
+        }
+    };
+
     float M = -INFINITY, Lam = 0.0f;
     f32x4 O[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    __syncthreads();
+    issue_k(0);
+
     for (int i = 0; i < nsplit; ++i) {
         const int t0 = i * kSplit;
-        float sv[kChunks][8];
+        __syncthreads();                 // K of split i landed; every wave is done with s_v
+        issue_v(i);
         // ---------------- scores
+        float sv[kChunks][8];
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-            __syncthreads();
+        for (int c = 0; c < kChunks; ++c) {
 #pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const int idx = tid + kThreads * it;
-                const int tl = idx >> 4;
-                const int ch = idx & 15;
-                const int tok = t0 + kHalf * hs + tl;
-                u32x4 v = zero_u32x4();
-                if (tok < L) {
-                    const int blk = btr[tok >> 4];
-                    if (blk >= 0 && blk < num_blocks)
-                        v = ld16(kc + (((int64_t)blk * Hkv + g) * kBlock + (tok & 15)) * kD + ch * 8);
-                }
-                st16(&s_buf[tl * kStride + ch * 8], v);
-            }
-            __syncthreads();
+            for (int th = 0; th < 2; ++th) {
+                const int row = 32 * c + score_row_token(col, th);
+                bf16x8 kf[4];
 #pragma unroll
-            for (int cl = 0; cl < 4; ++cl) {
-                const int c = 4 * hs + cl;
+                for (int dc = 0; dc < 4; ++dc)
+                    kf[dc] = *reinterpret_cast<const bf16x8*>(s_k + row * kD + (((4 * dc + grp) ^ kswz(row)) * 8));
+                const f32x4 acc = score_tile(kf, qf);
 #pragma unroll
-                for (int th = 0; th < 2; ++th) {
-                    const int tl = 32 * cl + score_row_token(col, th);
-                    bf16x8 kf[4];
-#pragma unroll
-                    for (int dc = 0; dc < 4; ++dc)
-                        kf[dc] = as_bf16x8(ld16(&s_buf[tl * kStride + 32 * dc + 8 * grp]));
-                    const f32x4 acc = score_tile(kf, qf);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 4 * th + r;
-                        const bool valid = (t0 + 32 * c + 8 * grp + j) <= pos;
-                        sv[c][j] = valid ? scaled_score(acc[r], scale_log2) : -INFINITY;
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 4 * th + r;
+                    const bool valid = (t0 + 32 * c + 8 * grp + j) <= pos;
+                    sv[c][j] = valid ? scaled_score(acc[r], scale_log2) : -INFINITY;
                 }
             }
         }
@@ -149,40 +184,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
             ls = lsum_add(ls, pf[c]);
         }
         ls = lsum_finish(ls);
-        // ---------------- values
+        __syncthreads();                 // V of split i landed; every wave is done with s_k
+        if (i + 1 < nsplit) issue_k(i + 1);
+        // ---------------- values (dims past the sequence end are zeroed: stale LDS)
         f32x4 o[8];
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-            __syncthreads();
+        for (int c = 0; c < kChunks; ++c) {
+            const int tok = t0 + 32 * c + 8 * grp;
+            const int b = 2 * c + (grp >> 1);
 #pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const int idx = tid + kThreads * it;
-                const int b = idx >> 8;             // block within the half split
-                const int rem = idx & 255;
-                const int d = rem >> 1;
-                const int half = rem & 1;
-                const int tok = t0 + kHalf * hs + 16 * b + 8 * half;
-                u32x4 v = zero_u32x4();
-                if (tok < L) {
-                    const int blk = btr[tok >> 4];
-                    if (blk >= 0 && blk < num_blocks) {
-                        v = ld16(vc + (((int64_t)blk * Hkv + g) * kD + d) * kBlock + 8 * half);
-                        if (tok + 8 > L) v = keep_first(v, L - tok);
-                    }
-                }
-                st16(&s_buf[d * kStride + 16 * b + 8 * half], v);
-            }
-            __syncthreads();
-#pragma unroll
-            for (int cl = 0; cl < 4; ++cl) {
-                const int c = 4 * hs + cl;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) {
-                    const bf16x8 vf = as_bf16x8(ld16(&s_buf[(16 * dt + col) * kStride + 32 * cl + 8 * grp]));
-                    o[dt] = pv_step(vf, pf[c], o[dt]);
-                }
+            for (int dt = 0; dt < 8; ++dt) {
+                const int d = 16 * dt + col;
+                u32x4 v = ld16(s_v + b * (kD * kBlock) + d * kBlock + vhalf(d, grp & 1) * 8);
+                if (tok + 8 > L) v = tok >= L ? zero_u32x4() : keep_first(v, L - tok);
+                o[dt] = pv_step(as_bf16x8(v), pf[c], o[dt]);
             }
         }
         // ---------------- fold
@@ -239,10 +256,10 @@ extern "C" int bi_attention_prefill(const void* q, int64_t ldq, const int32_t* q
         return BI_ERR_INVALID_ARGUMENT;
     const int G = Hq / Hkv;
     if (D != kD || !(G == 1 || G == 2 || G == 4 || G == 8 || G == 16) || S > 65535 || Hkv > 65535 ||
-        (int64_t)max_blocks * kBlock > (1 << 30))
+        max_blocks > kMaxBlocks)
         return BI_ERR_UNSUPPORTED;
     if (S == 0 || T == 0 || max_q_len == 0) return BI_OK;
-    const int QT = 64 / G;
+    const int QT = kRows / G;
     const int ntiles = (max_q_len + QT - 1) / QT;
     hipLaunchKernelGGL(prefill_kernel, dim3(ntiles, Hkv, S), dim3(kThreads), 0, (hipStream_t)stream,
                        (const uint16_t*)q, ldq, q_start, kv_lens, (const uint16_t*)k_cache,

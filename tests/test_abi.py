@@ -142,6 +142,8 @@ def test_attention_validation(L):
     assert pre(*bad) == 2                                     # group 3 unsupported
     bad = list(pargs); bad[12] = 0
     assert pre(*bad) == 0                                     # T == 0
+    bad = list(pargs); bad[8] = 4097
+    assert pre(*bad) == 2                                     # block table wider than 4096
 
 
 def test_probe_copy_validation(L):
