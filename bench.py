@@ -57,8 +57,13 @@ def src_hash(*names):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_src: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+GEMM_SOURCES = ("gemm.hip", "gemm_kernel.hpp", "bi_common.hpp")
+COPY_PROBE_BYTES = 512 << 20
+
+
+def traffic_from_profile():
+    """HBM bytes per bi_matmul launch of the sweep, from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE scaled by the copy probe), if it
     was taken on the current kernel source; else None."""
     p = os.path.join(ROOT, "profiles", "gemm_llama_sweep_counters.json")
     try:
@@ -66,7 +71,7 @@ def traffic_from_profile(kernel_src: str):
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("source_hash") != src_hash(kernel_src):
+    if d.get("source_hash") != src_hash(*GEMM_SOURCES):
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -231,9 +236,17 @@ def main():
     # the replayed sweep ends with M=2048: its first rows must equal the eager run bit for bit
     graph_matches_eager = bool(torch.equal(C[14336][:64].view(torch.int16), ref_c.view(torch.int16)))
     # per-launch durations of bi_matmul: eager passes of the same sweep, a HIP
-    # event pair around every launch
+    # event pair around every launch.  Each pass is queued behind a few graph
+    # replays of the sweep, so the host has queued every launch before the GPU
+    # reaches it and an event pair brackets the kernel, not host launch gaps.
+    head = 3
+    host_enqueue_ms = []
     for _ in range(max(2, args.steps // 2)):
+        for _ in range(head):
+            graphs["phase1"].replay()
+        th = time.perf_counter()
         phase1(True)
+        host_enqueue_ms.append((time.perf_counter() - th) * 1e3)
     torch.cuda.synchronize()
 
     def total_ms(pairs):
@@ -245,7 +258,8 @@ def main():
     gemm_flops = sum(r[2] for r in rec["gemm"])
     achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
     n_launch = len(rec["gemm"])
-    traffic = traffic_from_profile("gemm.hip")
+    traffic = traffic_from_profile()
+    gemm_bytes = sum(2 * (M * H + N * H + M * N) for (_, _, _, M, N) in rec["gemm"])
 
     # per-M table (median over steps)
     per = {}
@@ -292,6 +306,11 @@ def main():
             "traffic": traffic,
             "launches": n_launch, "avg_launch_us": round(gemm_ms * 1e3 / n_launch, 3),
             "flops_per_launch_avg": gemm_flops / n_launch,
+            "algorithmic_bytes_per_launch_avg": gemm_bytes / n_launch,
+            "timing": (f"event pair per launch in eager sweeps queued behind {head} graph replays "
+                       f"({head * phase1_ms:.1f} ms of GPU work); host queued each sweep in "
+                       f"{max(host_enqueue_ms):.1f} ms at most"),
+            "source_hash": src_hash(*GEMM_SOURCES),
         },
         "gemm_sweep": sweep,
         "rmsnorm": {"GB/s": round(rms_bytes / (rms_ms * 1e-3) / 1e9, 1),
@@ -310,6 +329,25 @@ def main():
         tf = pre_flops / (pms * 1e-3) / 1e12
         result["prefill"] = {"P": P_PRE, "us": round(pms * 1e3, 1), "TFLOP/s": round(tf, 2),
                              "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    # copy probe: a plain device copy of known size, the reference for what the
+    # HBM traffic counters read per byte, and the copy bandwidth this machine reaches
+    src = torch.empty(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    ops.bi_probe_copy(src, dst)
+    torch.cuda.synchronize()
+    cs, ce = E(), E()
+    cs.record(stream)
+    for _ in range(5):
+        ops.bi_probe_copy(src, dst)
+    ce.record(stream)
+    torch.cuda.synchronize()
+    copy_us = cs.elapsed_time(ce) * 1e3 / 5
+    result["copy_probe"] = {"bytes_read": COPY_PROBE_BYTES, "bytes_written": COPY_PROBE_BYTES,
+                            "us": round(copy_us, 1),
+                            "GB/s": round(2 * COPY_PROBE_BYTES / (copy_us * 1e-6) / 1e9, 1)}
+    del src, dst
 
     # non-invariant vendor GEMM (hipBLASLt through torch) on the same sweep, context only
     try:

@@ -20,8 +20,10 @@
 // The one configuration (chosen by measuring the whole M = 1..2048 sweep of
 // Llama-8B projections on MI355X; small M is weight-streaming, large M is
 // MFMA/L2 bound, and one tile has to serve both):
-//   * workgroup tile 64 (m) x 64 (n) x 256 (k), 256 threads = 4 wavefronts in
-//     a 2x2 arrangement, each wavefront 32x32 outputs as 2x2 MFMA tiles;
+//   * workgroup tile 64 (m) x 64 (n) x 256 (k), 512 threads = 8 wavefronts in
+//     a 4 (m) x 2 (n) arrangement, each wavefront 16x32 outputs as 1x2 MFMA
+//     tiles (eight wavefronts keep more loads in flight per CU than four,
+//     which is what the weight-streaming small-M shapes are bound by);
 //   * operands go global -> LDS with global_load_lds_dwordx4 (no register
 //     staging), two stages, so one 64 KB stage is in flight while the other is
 //     consumed; a row's 256-wide k slice is 512 contiguous bytes in HBM;

@@ -12,7 +12,7 @@ namespace {
 constexpr int kBM = 64;
 constexpr int kBN = 64;
 constexpr int kBK = 256;
-constexpr int kWM = 2;
+constexpr int kWM = 4;
 constexpr int kWN = 2;
 constexpr int kStages = 2;
 constexpr int kGroup = 4;                         // m-tiles per band of the tile order
