@@ -8,6 +8,9 @@ under profiles/.
     python -m invariant_bi_rmsnorm_amd.profile_summary traffic FETCH_DIR WRITE_DIR OUT.md OUT.json \
         --cmd-fetch "..." --cmd-write "..."
 
+    # MFMA utilisation (MfmaUtil, MfmaFlopsBF16) next to kernel durations
+    python -m invariant_bi_rmsnorm_amd.profile_summary mfma DIR TRACE_DIR OUT.md --cmd "..."
+
     # any other counters (per kernel, per dispatch averages)
     python -m invariant_bi_rmsnorm_amd.profile_summary counters DIR OUT.md --cmd "..." --title "..."
 
@@ -86,7 +89,17 @@ def read_counters(d):
     return out
 
 
-def traffic(fetch_dir, write_dir, out_md, out_json, cmd_fetch, cmd_write):
+def avg_durations_us(trace_dir):
+    """{kernel: average duration in microseconds} from a --kernel-trace --stats run"""
+    out = {}
+    for r in csv.DictReader(open(_one("*kernel_stats.csv", trace_dir))):
+        k = short(r["Name"])
+        if k in KERNELS:
+            out[k] = float(r["AverageNs"]) / 1e3
+    return out
+
+
+def traffic(fetch_dir, write_dir, out_md, out_json, cmd_fetch, cmd_write, trace_dir=None):
     fe = read_counters(fetch_dir)
     wr = read_counters(write_dir)
     cf = fe["copy_kernel"]["FETCH_SIZE"]
@@ -102,8 +115,9 @@ def traffic(fetch_dir, write_dir, out_md, out_json, cmd_fetch, cmd_write):
              f"Calibration on the copy probe ({COPY_PROBE_BYTES >> 20} MiB read + written): "
              f"FETCH_SIZE read {cf[0]:.0f} KiB, WRITE_SIZE {cw[0]:.0f} KiB; "
              f"bytes = KiB x 1024 x {f_fetch:.4f} (fetch), x {f_write:.4f} (write).", "",
-             "| kernel | dispatches | fetch MB/launch | write MB/launch | traffic MB/launch |",
-             "|---|---|---|---|---|"]
+             "| kernel | dispatches | fetch MB/launch | write MB/launch | traffic MB/launch | avg us | HBM GB/s |",
+             "|---|---|---|---|---|---|---|"]
+    dur = avg_durations_us(trace_dir) if trace_dir else {}
     summary = {}
     for k in KERNELS:
         a, b = fe.get(k, {}).get("FETCH_SIZE", []), wr.get(k, {}).get("WRITE_SIZE", [])
@@ -112,7 +126,10 @@ def traffic(fetch_dir, write_dir, out_md, out_json, cmd_fetch, cmd_write):
         fm = sum(a) / len(a) * 1024 * f_fetch
         wm = sum(b) / len(b) * 1024 * f_write
         summary[k] = {"dispatches": len(a), "fetch_bytes": fm, "write_bytes": wm, "traffic_bytes": fm + wm}
-        lines.append(f"| {k} | {len(a)} | {fm / 1e6:.2f} | {wm / 1e6:.2f} | {(fm + wm) / 1e6:.2f} |")
+        us = dur.get(k)
+        rate = f"{(fm + wm) / (us * 1e-6) / 1e9:.0f}" if us else ""
+        lines.append(f"| {k} | {len(a)} | {fm / 1e6:.2f} | {wm / 1e6:.2f} | {(fm + wm) / 1e6:.2f} | "
+                     f"{us if us is None else round(us, 2)} | {rate} |")
     g = summary.get("gemm_kernel")
     doc = {"source_hash": src_hash(*GEMM_SOURCES), "kernels": summary,
            "calibration": {"fetch_factor": f_fetch, "write_factor": f_write}}
@@ -145,6 +162,30 @@ def traffic(fetch_dir, write_dir, out_md, out_json, cmd_fetch, cmd_write):
         f.write("\n")
 
 
+def mfma_md(d, trace_dir, out, cmd):
+    cs = read_counters(d)
+    dur = avg_durations_us(trace_dir)
+    lines = ["# MFMA utilisation per kernel (rocprofv3 MfmaUtil, MfmaFlopsBF16), bench.py phases", "",
+             "Command (from the repository root, one MI355X):", "", "```", cmd, "```", "",
+             "MfmaUtil = busy cycles of the MFMA units / (GPU active cycles x SIMDs), in percent, "
+             "mean over dispatches.  MFMA TFLOP/s = counted bf16 MFMA flops per dispatch / the kernel's "
+             "average duration from the kernel trace of the same workload.", "",
+             "| kernel | dispatches | MfmaUtil % | MFMA GFLOP/dispatch | avg us | MFMA TFLOP/s |",
+             "|---|---|---|---|---|---|"]
+    for k in KERNELS:
+        if k not in cs or "MfmaUtil" not in cs[k]:
+            continue
+        u = cs[k]["MfmaUtil"]
+        f = cs[k].get("MfmaFlopsBF16", [])
+        fl = sum(f) / len(f) if f else 0.0
+        us = dur.get(k)
+        tf = f"{fl / (us * 1e-6) / 1e12:.1f}" if us and fl else ""
+        lines.append(f"| {k} | {len(u)} | {sum(u) / len(u):.1f} | {fl / 1e9:.3f} | "
+                     f"{'' if us is None else round(us, 2)} | {tf} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def counters_md(d, out, cmd, title):
     cs = read_counters(d)
     names = sorted({c for k in cs for c in cs[k]})
@@ -169,6 +210,10 @@ def main():
     for a in ("fetch_dir", "write_dir", "out_md", "out_json"):
         t.add_argument(a)
     t.add_argument("--cmd-fetch", required=True), t.add_argument("--cmd-write", required=True)
+    t.add_argument("--trace-dir")
+    mf = sub.add_parser("mfma")
+    mf.add_argument("dir"), mf.add_argument("trace_dir"), mf.add_argument("out")
+    mf.add_argument("--cmd", required=True)
     c = sub.add_parser("counters")
     c.add_argument("dir"), c.add_argument("out"), c.add_argument("--cmd", required=True)
     c.add_argument("--title", required=True)
@@ -176,7 +221,9 @@ def main():
     if a.what == "stats":
         stats_md(a.dir, a.out, a.cmd, a.title)
     elif a.what == "traffic":
-        traffic(a.fetch_dir, a.write_dir, a.out_md, a.out_json, a.cmd_fetch, a.cmd_write)
+        traffic(a.fetch_dir, a.write_dir, a.out_md, a.out_json, a.cmd_fetch, a.cmd_write, a.trace_dir)
+    elif a.what == "mfma":
+        mfma_md(a.dir, a.trace_dir, a.out, a.cmd)
     else:
         counters_md(a.dir, a.out, a.cmd, a.title)
 
