@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--skip", default="", help="comma list of phases to skip: decode,prefill")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the supplementary points (RMSNorm 1 GiB, decode S sweep, prefill P sweep)")
     return ap.parse_args()
 
 
@@ -275,6 +277,9 @@ def main():
                       "frac_mfma_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4),
                       "frac_roofline": round(roof_t / t, 4)})
 
+    roof_total = sum(max(2 * M * N * H / (PEAK_BF16_TFLOPS * 1e12), 2 * (M * H + N * H + M * N) / (PEAK_HBM_GBS * 1e9))
+                     for (M, N) in per)
+    meas_total = sum(float(np.median(ts)) * 1e-3 for ts in per.values())
     rms_ms = total_ms(rec["rms"])
     rms_bytes = sum(4 * M * H + 2 * H for (_, _, M) in rec["rms"])
 
@@ -307,6 +312,7 @@ def main():
             "launches": n_launch, "avg_launch_us": round(gemm_ms * 1e3 / n_launch, 3),
             "flops_per_launch_avg": gemm_flops / n_launch,
             "algorithmic_bytes_per_launch_avg": gemm_bytes / n_launch,
+            "frac_of_min_roofline": round(roof_total / meas_total, 4),
             "timing": (f"event pair per launch in eager sweeps queued behind {head} graph replays "
                        f"({head * phase1_ms:.1f} ms of GPU work); host queued each sweep in "
                        f"{max(host_enqueue_ms):.1f} ms at most"),
@@ -329,6 +335,73 @@ def main():
         tf = pre_flops / (pms * 1e-3) / 1e12
         result["prefill"] = {"P": P_PRE, "us": round(pms * 1e3, 1), "TFLOP/s": round(tf, 2),
                              "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    # ------------------------------------------------------------ supplementary points
+    # (outside the step; each timed as a HIP graph of back-to-back launches)
+    def graph_us(fn, reps):
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            for _ in range(reps):
+                fn()
+        gph.replay()
+        torch.cuda.synchronize()
+        a, b = E(), E()
+        a.record(stream)
+        gph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    if not args.no_extra:
+        extra = {}
+        log("supplementary: RMSNorm 65536 x 4096")
+        Mbig = 65536
+        xb = torch.randn((Mbig, H), device=dev, dtype=torch.float32).to(torch.bfloat16)
+        yb = torch.empty_like(xb)
+        us = graph_us(lambda: ops.bi_rmsnorm(xb, wn, I.LLAMA_EPS, y=yb, want_rstd=False), 5)
+        byt = 4 * Mbig * H + 2 * H
+        extra["rmsnorm_65536x4096"] = {"us": round(us, 1), "bytes": byt,
+                                       "GB/s": round(byt / (us * 1e-6) / 1e9, 1),
+                                       "frac_hbm": round(byt / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del xb, yb
+        if "decode" not in skip:
+            log("supplementary: decode S sweep")
+            rows = []
+            for Sd in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+                ls = lens[:Sd]
+                ml = int(ls.max())
+                us = graph_us(lambda: ops.bi_attention_decode(qd[:Sd], kc, vc, tbl[:Sd], lens_d[:Sd], ml, scale,
+                                                              ws=ws, out=dec_out[:Sd]), 10)
+                byt = (int(ls.sum()) * I.ATT_HKV * I.ATT_D * 4 + Sd * I.ATT_HQ * I.ATT_D * 4
+                       + 4 * int(sum(-(-int(L) // 16) for L in ls)))
+                rows.append({"S": Sd, "kv_tokens": int(ls.sum()), "us": round(us, 2),
+                             "GB/s": round(byt / (us * 1e-6) / 1e9, 1)})
+            extra["decode_S_sweep"] = {"rows": rows, "includes": "split + combine (no append)",
+                                       "note": "aggregate KV below the 256 MB MALL at small S"}
+        if "prefill" not in skip:
+            log("supplementary: prefill P sweep")
+            rows = []
+            for P in (512, 2048, 8192):
+                qsP = torch.tensor([0, P], dtype=torch.int32, device=dev)
+                lP = torch.tensor([P], dtype=torch.int32, device=dev)
+                us = graph_us(lambda: ops.bi_attention_prefill(pq[:P], qsP, lP, pk, pv, ptbl, P, scale,
+                                                               out=pout[:P]), 3)
+                fl = 4 * I.ATT_HQ * I.ATT_D * (P * (P + 1) // 2)
+                rows.append({"P": P, "us": round(us, 1), "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1)})
+            # the 8192-token prompt as four 2048-token chunks over the growing cache
+            CH = 2048
+            qs_ch = torch.tensor([0, CH], dtype=torch.int32, device=dev)
+            l_ch = [torch.tensor([(c + 1) * CH], dtype=torch.int32, device=dev) for c in range(P_PRE // CH)]
+
+            def chunked():
+                for c in range(P_PRE // CH):
+                    ops.bi_attention_prefill(pq[c * CH:(c + 1) * CH], qs_ch, l_ch[c], pk, pv, ptbl, CH, scale,
+                                             out=pout[c * CH:(c + 1) * CH])
+            us = graph_us(chunked, 2)
+            rows.append({"P": P_PRE, "chunks": CH, "us": round(us, 1),
+                         "TFLOP/s": round(pre_flops / (us * 1e-6) / 1e12, 1)})
+            extra["prefill_P_sweep"] = rows
+        result["supplementary"] = extra
 
     # copy probe: a plain device copy of known size, the reference for what the
     # HBM traffic counters read per byte, and the copy bandwidth this machine reaches

@@ -232,9 +232,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 // per head dim).  Splits are taken in chunks of kFoldChunk: the threads load
 // the chunk's (m, l) into LDS, one thread runs the scalar recurrence of the
 // fold in split order and leaves each split's weights (a, b) in LDS, then every
-// thread applies them to its dim.  Same operations, same order as a plain left
-// fold -- only the loads are batched.
+// thread applies them to its dim.  Each thread's partial values are loaded
+// kPre splits at a time, the first batch before the scalar recurrence, so a
+// chain of n splits waits on memory about n / kPre times instead of n.  Same
+// operations, same order as a plain left fold -- only the loads are batched.
 constexpr int kFoldChunk = 256;
+constexpr int kPre = 32;
 
 __global__ __launch_bounds__(kD) void decode_combine_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ kv_lens, int cap, int Hq,
@@ -256,10 +259,14 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
     float M = 0.f, Lam = 0.f, O = 0.f;
     for (int c0 = 0; c0 < n; c0 += kFoldChunk) {
         const int cn = min(kFoldChunk, n - c0);
+        const float* cb = base + (int64_t)c0 * (kD + 2);
         for (int i = d; i < cn; i += kD) {
-            s_m[i] = base[(int64_t)(c0 + i) * (kD + 2)];
-            s_l[i] = base[(int64_t)(c0 + i) * (kD + 2) + 1];
+            s_m[i] = cb[(int64_t)i * (kD + 2)];
+            s_l[i] = cb[(int64_t)i * (kD + 2) + 1];
         }
+        float v[kPre];
+#pragma unroll
+        for (int j = 0; j < kPre; ++j) v[j] = j < cn ? cb[(int64_t)j * (kD + 2) + 2 + d] : 0.f;
         __syncthreads();
         if (d == 0) {
             int i = 0;
@@ -272,13 +279,21 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
             s_lam = Lam;
         }
         __syncthreads();
-        int i = 0;
-        if (c0 == 0) {
-            O = base[2 + d];
-            i = 1;
+        for (int i0 = 0; i0 < cn; i0 += kPre) {
+            if (i0 > 0) {
+#pragma unroll
+                for (int j = 0; j < kPre; ++j)
+                    v[j] = i0 + j < cn ? cb[(int64_t)(i0 + j) * (kD + 2) + 2 + d] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < kPre; ++j) {
+                const int i = i0 + j;
+                if (i < cn) {
+                    if (c0 == 0 && i == 0) O = v[j];
+                    else O = fold_value(O, v[j], s_a[i], s_b[i]);
+                }
+            }
         }
-#pragma unroll 8
-        for (; i < cn; ++i) O = fold_value(O, base[(int64_t)(c0 + i) * (kD + 2) + 2 + d], s_a[i], s_b[i]);
         __syncthreads();          // the chunk's LDS is reused by the next chunk
     }
     *o = (uint16_t)f32_to_bf16_rne(finish_value(O, s_lam));
