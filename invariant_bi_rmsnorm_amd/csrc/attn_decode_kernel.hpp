@@ -229,25 +229,30 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 }
 
 // Fold of the split partials of one (sequence, query head), 128 threads (one
-// per head dim).  Splits are taken in chunks of kFoldChunk: the threads load
-// the chunk's (m, l) into LDS, one thread runs the scalar recurrence of the
-// fold in split order and leaves each split's weights (a, b) in LDS, then every
-// thread applies them to its dim.  Each thread's partial values are loaded
-// kPre splits at a time, the first batch before the scalar recurrence, so a
-// chain of n splits waits on memory about n / kPre times instead of n.  Same
-// operations, same order as a plain left fold -- only the loads are batched.
-constexpr int kFoldChunk = 256;
+// per head dim), splits taken 128 at a time (thread t owns split c0 + t of the
+// chunk for the scalar part).  The left fold over splits i = 0, 1, ... is
+//   M_i = max(M_{i-1}, m_i),  a_i = exp2(M_{i-1} - M_i),  b_i = exp2(m_i - M_i),
+//   L_i = L_{i-1} a_i + l_i b_i,  O_i = O_{i-1} a_i + o_i b_i,
+// starting from split 0's own (m, l, o).  The running maxima M_i are a prefix
+// maximum, which is exact whatever the grouping, so they are formed with a
+// wavefront scan; each thread then computes its split's (a_i, b_i) with exactly
+// the operations of fold_scalars, and every thread runs the two rounding
+// chains (L and its dim of O) in split order.  The bits equal those of the
+// sequential fold_scalars / fold_value recurrence the prefill kernel runs in
+// registers.  Partial values are loaded kPre splits at a time.
+constexpr int kFoldChunk = kD;
 constexpr int kPre = 32;
 
 __global__ __launch_bounds__(kD) void decode_combine_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ kv_lens, int cap, int Hq,
     int max_splits, int split_len, uint16_t* __restrict__ out, int64_t ldo)
 {
-    __shared__ float s_m[kFoldChunk], s_l[kFoldChunk], s_a[kFoldChunk], s_b[kFoldChunk];
-    __shared__ float s_lam;
+    __shared__ float s_a[kFoldChunk], s_b[kFoldChunk], s_l[kFoldChunk];
+    __shared__ float s_wmax[2];
     const int s = blockIdx.y;
     const int h = blockIdx.x;
     const int d = threadIdx.x;
+    const int lane = d & 63;
     const int L = clamp_len(kv_lens[s], cap);
     const int n = (L + split_len - 1) / split_len;
     uint16_t* o = out + (int64_t)s * ldo + (int64_t)h * kD + d;
@@ -256,29 +261,38 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
         return;
     }
     const float* base = ws + ((int64_t)s * Hq + h) * max_splits * (kD + 2);
-    float M = 0.f, Lam = 0.f, O = 0.f;
+    float Mprev = -INFINITY, Lam = 0.f, O = 0.f;
     for (int c0 = 0; c0 < n; c0 += kFoldChunk) {
         const int cn = min(kFoldChunk, n - c0);
         const float* cb = base + (int64_t)c0 * (kD + 2);
-        for (int i = d; i < cn; i += kD) {
-            s_m[i] = cb[(int64_t)i * (kD + 2)];
-            s_l[i] = cb[(int64_t)i * (kD + 2) + 1];
-        }
+        // ---- scalar part: thread d owns split c0 + d
+        const bool own = d < cn;
+        const float mi = own ? cb[(int64_t)d * (kD + 2)] : -INFINITY;
+        const float li = own ? cb[(int64_t)d * (kD + 2) + 1] : 0.f;
         float v[kPre];
 #pragma unroll
         for (int j = 0; j < kPre; ++j) v[j] = j < cn ? cb[(int64_t)j * (kD + 2) + 2 + d] : 0.f;
-        __syncthreads();
-        if (d == 0) {
-            int i = 0;
-            if (c0 == 0) {            // the state starts as split 0's own (m, l, o)
-                M = s_m[0];
-                Lam = s_l[0];
-                i = 1;
-            }
-            for (; i < cn; ++i) fold_scalars(M, Lam, s_m[i], s_l[i], s_a[i], s_b[i]);
-            s_lam = Lam;
+        float run = mi;                                   // inclusive prefix max inside the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float t = __shfl_up(run, off, 64);
+            if (lane >= off) run = fmaxf(run, t);
         }
+        if (lane == 63) s_wmax[d >> 6] = run;
         __syncthreads();
+        if (d >= 64) run = fmaxf(s_wmax[0], run);
+        const float Mi = fmaxf(Mprev, run);               // M_{c0 + d}
+        float Mim1 = __shfl_up(Mi, 1, 64);                // M_{c0 + d - 1}
+        if (lane == 0) Mim1 = d == 0 ? Mprev : fmaxf(Mprev, s_wmax[0]);
+        if (own) {
+            s_a[d] = hw_exp2(Mim1 - Mi);
+            s_b[d] = hw_exp2(mi - Mi);
+            s_l[d] = li;
+        }
+        // carry: M after the chunk's last split
+        const float chunk_max = cn > 64 ? fmaxf(s_wmax[0], s_wmax[1]) : s_wmax[0];
+        __syncthreads();
+        // ---- the two chains, in split order
         for (int i0 = 0; i0 < cn; i0 += kPre) {
             if (i0 > 0) {
 #pragma unroll
@@ -289,14 +303,20 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
             for (int j = 0; j < kPre; ++j) {
                 const int i = i0 + j;
                 if (i < cn) {
-                    if (c0 == 0 && i == 0) O = v[j];
-                    else O = fold_value(O, v[j], s_a[i], s_b[i]);
+                    if (c0 == 0 && i == 0) {
+                        Lam = s_l[0];
+                        O = v[j];
+                    } else {
+                        Lam = Lam * s_a[i] + s_l[i] * s_b[i];
+                        O = fold_value(O, v[j], s_a[i], s_b[i]);
+                    }
                 }
             }
         }
+        Mprev = fmaxf(Mprev, chunk_max);
         __syncthreads();          // the chunk's LDS is reused by the next chunk
     }
-    *o = (uint16_t)f32_to_bf16_rne(finish_value(O, s_lam));
+    *o = (uint16_t)f32_to_bf16_rne(finish_value(O, Lam));
 }
 
 static inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }

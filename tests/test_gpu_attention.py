@@ -188,3 +188,20 @@ def test_prefill_varlen_batch_invariance(ops):
         cache1, table1 = make_cache(g, [kvs[s]])
         alone = prefill(ops, cache1, table1, qs[s], np.array([0, T[s]], np.int32), L[s:s + 1])
         assert np.array_equal(batch[q_start[s]:q_start[s + 1]], alone), f"s={s}"
+
+
+def test_decode_long_sequences_fold_over_chunks(ops, orc):
+    """Sequences longer than 128 splits (the combine folds them 128 at a time):
+    decode equals the prefill row at the same length bit for bit, and matches
+    the oracle."""
+    g = np.random.default_rng(6)
+    for L in (32769, 40000):
+        log(f"long decode L={L}")
+        k, v = I.kv_sequence(I.TAG_DECODE, 6, L, L)
+        q = I.queries(I.TAG_DECODE, 6 + L, 1)
+        cache, table = make_cache(g, [(k, v)])
+        d = decode(ops, cache, table, q, np.array([L], np.int32))
+        p = prefill(ops, cache, table, q, np.array([0, 1], np.int32), np.array([L], np.int32))
+        assert np.array_equal(d[0], p[0])
+        o16, o64 = oracle_decode(orc, q[0], k, v)
+        check_bf16(d[0], o64, f"decode L={L}", axis=None)
