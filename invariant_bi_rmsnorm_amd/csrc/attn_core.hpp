@@ -61,21 +61,20 @@ __device__ __forceinline__ f32x4 score_tile(const bf16x8 kf[4], const bf16x8 qf[
 
 __device__ __forceinline__ float scaled_score(float acc, float scale_log2) { return acc * scale_log2; }
 
-// bf16 weight of one token, given the split max of its row.
-__device__ __forceinline__ uint32_t weight_bf16(float s, float m, bool valid)
+// Weight of one token before rounding, given the split max of its row.
+__device__ __forceinline__ float weight_f32(float s, float m, bool valid)
 {
-    const float p = valid ? hw_exp2(s - m) : 0.0f;
-    return f32_to_bf16_rne(p);
+    return valid ? hw_exp2(s - m) : 0.0f;
 }
 
-// Pack 8 weights (j = 0..7) into one MFMA operand.
-__device__ __forceinline__ bf16x8 pack_weights(const uint32_t w[8])
+// Round 8 weights (j = 0..7) to bf16 and pack them into one MFMA operand.
+__device__ __forceinline__ bf16x8 pack_weights(const float p[8])
 {
     u32x4 v;
-    v[0] = w[0] | (w[1] << 16);
-    v[1] = w[2] | (w[3] << 16);
-    v[2] = w[4] | (w[5] << 16);
-    v[3] = w[6] | (w[7] << 16);
+    v[0] = pack_bf16x2(p[0], p[1]);
+    v[1] = pack_bf16x2(p[2], p[3]);
+    v[2] = pack_bf16x2(p[4], p[5]);
+    v[3] = pack_bf16x2(p[6], p[7]);
     return as_bf16x8(v);
 }
 

@@ -190,10 +190,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             const int c = 2 * wave + cc;
-            uint32_t wv[8];
+            float wv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                wv[j] = weight_bf16(sv[cc][j], m, (t0 + 32 * c + 8 * grp + j) < L);
+                wv[j] = weight_f32(sv[cc][j], m, (t0 + 32 * c + 8 * grp + j) < L);
             st16(&s_pt[col * kPtStride + 32 * c + 8 * grp], as_u32x4(pack_weights(wv)));
         }
         __syncthreads();

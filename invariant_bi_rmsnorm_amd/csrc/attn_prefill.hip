@@ -177,9 +177,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         float ls = 0.0f;
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
-            uint32_t wv[8];
+            float wv[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) wv[j] = weight_bf16(sv[c][j], mx, (t0 + 32 * c + 8 * grp + j) <= pos);
+            for (int j = 0; j < 8; ++j) wv[j] = weight_f32(sv[c][j], mx, (t0 + 32 * c + 8 * grp + j) <= pos);
             pf[c] = pack_weights(wv);
             ls = lsum_add(ls, pf[c]);
         }

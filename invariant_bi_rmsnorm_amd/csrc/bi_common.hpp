@@ -5,7 +5,11 @@
 //   * built with -ffp-contract=off and without fast-math: every + and * is an
 //     IEEE operation rounded on its own; fused multiply-adds appear only where
 //     written explicitly with __fmaf_rn;
-//   * fp32 -> bf16 is round-to-nearest-even done on the bit pattern here;
+//   * fp32 -> bf16 is round-to-nearest-even by the gfx950 instruction
+//     v_cvt_pk_bf16_f32 (two values per instruction); compared on the device
+//     against round-to-nearest-even done on the bit pattern for all 2^32 fp32
+//     inputs: identical, NaNs included (a NaN keeps its sign and top payload
+//     bits and comes out quiet);
 //   * exp2 is the hardware v_exp_f32 (one instruction, deterministic);
 //   * no atomics anywhere: every reduction has one fixed order.
 #pragma once
@@ -25,18 +29,17 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h16)
     return __uint_as_float(h16 << 16);
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;   // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+// two fp32 -> packed bf16 (lo in bits 0..15), round to nearest even
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.0f) & 0xffffu; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }

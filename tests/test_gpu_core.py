@@ -223,3 +223,40 @@ def test_argmax_matches_oracle(ops, orc):
     ids = ops.bi_argmax(torch.from_numpy(x).cuda()).cpu().numpy()
     assert np.array_equal(ids, orc.argmax(x))
     assert ids[13] == -1
+
+
+def test_bf16_rounding_edges(ops, orc):
+    """Every bf16 store of the library rounds to nearest even.  Checked through
+    bi_add, whose fp32 sum of the two bf16 inputs below is exact, so the only
+    rounding is the store: ties to even (also with a carry into the exponent
+    and at the smallest normal exponents), round up past half, overflow of a
+    tie to infinity, signed zeros; NaN stays NaN."""
+    pairs = [
+        (0x3F80, 0x3B80),   # 1 + 2^-8: tie -> 1 (even)
+        (0x3F81, 0x3B80),   # (1 + 2^-7) + 2^-8: tie -> 1 + 2^-6 (even)
+        (0x3F80, 0x3BC0),   # 1 + 1.5 * 2^-8: above half -> 1 + 2^-7
+        (0x3FFF, 0x3B80),   # (2 - 2^-7) + 2^-8: tie, carry -> 2
+        (0xBFFF, 0xBB80),   # the same, negative -> -2
+        (0x0100, 0x0001),   # 2^-125 + 2^-133: tie at quantum 2^-132 -> 2^-125
+        (0x0101, 0x0001),   # (2^-125 + 2^-132) + 2^-133: tie -> 2^-125 + 2^-131
+        (0x0001, 0x0001),   # bf16 subnormals add exactly -> 2^-132
+        (0x007F, 0x0001),   # largest subnormal + smallest -> smallest normal
+        (0x7F7F, 0x7B00),   # max finite + half ulp: tie -> +inf (even)
+        (0x7F7F, 0x7A80),   # max finite + quarter ulp -> max finite
+        (0x8000, 0x8000),   # -0 + -0 -> -0
+        (0x8000, 0x0000),   # -0 + +0 -> +0
+        (0x7F80, 0x3F80),   # inf + 1 -> inf
+    ]
+    a = np.zeros(24, np.uint16)
+    b = np.zeros(24, np.uint16)
+    for i, (x, y) in enumerate(pairs):
+        a[i], b[i] = x, y
+    got = host_bits(ops.bi_add(dev_bf16(a), dev_bf16(b)))
+    assert np.array_equal(got, orc.add(a, b))
+    assert got[0] == 0x3F80 and got[3] == 0x4000 and got[9] == 0x7F80 and got[11] == 0x8000
+    # NaN in, NaN out (payload bits are not compared)
+    n = np.zeros(8, np.uint16)
+    n[0] = 0x7FC1
+    n[1] = 0xFF81
+    out = host_bits(ops.bi_add(dev_bf16(n), dev_bf16(np.full(8, 0x3F80, np.uint16))))
+    assert all((int(v) & 0x7F80) == 0x7F80 and (int(v) & 0x7F) != 0 for v in out[:2])
