@@ -21,6 +21,8 @@
 // 0 and the arithmetic per split does not depend on which or how many other
 // rows share the call, a row's output is the same whether its prompt arrived
 // in one piece or in chunks, and equals decode at the same length.
+#include <type_traits>
+
 #include "attn_core.hpp"
 
 using namespace bi_attn;
@@ -91,6 +93,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const bool cvalid = tq < Ts;
     const int pos = cvalid ? p0 + tq : -1;
     const int last = min(Ts - 1, qt * QT + QT - 1);
+    // rows of this wavefront: tokens tq0 .. tq0 + tpw - 1 of the chunk
+    const int tq0 = qt * QT + wave * tpw;
+    const bool wave_full = tq0 + tpw - 1 < Ts;       // every column is a real row
+    const int wave_pos0 = p0 + tq0;                  // the smallest position among them
     const int nsplit = (p0 + last) / kSplit + 1;
 
     bf16x8 qf[4];
@@ -146,44 +152,56 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         const int t0 = i * kSplit;
         __syncthreads();                 // K of split i landed; every wave is done with s_v
         issue_v(i);
-        // ---------------- scores
-        float sv[kChunks][8];
+        // ---------------- scores, max, weights, sum.  When every row of the
+        // wavefront sees the whole split (all but the diagonal splits) the
+        // causal mask is dropped: same values, fewer instructions.
+        bf16x8 pf[kChunks];
+        float mx = -INFINITY, ls = 0.0f;
+        auto softmax_part = [&](auto masked) {
+            constexpr bool kMasked = decltype(masked)::value;
+            float sv[kChunks][8];
 #pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
+            for (int c = 0; c < kChunks; ++c) {
 #pragma unroll
-            for (int th = 0; th < 2; ++th) {
-                const int row = 32 * c + score_row_token(col, th);
-                bf16x8 kf[4];
+                for (int th = 0; th < 2; ++th) {
+                    const int row = 32 * c + score_row_token(col, th);
+                    bf16x8 kf[4];
 #pragma unroll
-                for (int dc = 0; dc < 4; ++dc)
-                    kf[dc] = *reinterpret_cast<const bf16x8*>(s_k + row * kD + (((4 * dc + grp) ^ kswz(row)) * 8));
-                const f32x4 acc = score_tile(kf, qf);
+                    for (int dc = 0; dc < 4; ++dc)
+                        kf[dc] = *reinterpret_cast<const bf16x8*>(s_k + row * kD + (((4 * dc + grp) ^ kswz(row)) * 8));
+                    const f32x4 acc = score_tile(kf, qf);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 4 * th + r;
-                    const bool valid = (t0 + 32 * c + 8 * grp + j) <= pos;
-                    sv[c][j] = valid ? scaled_score(acc[r], scale_log2) : -INFINITY;
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 4 * th + r;
+                        if constexpr (kMasked) {
+                            const bool valid = (t0 + 32 * c + 8 * grp + j) <= pos;
+                            sv[c][j] = valid ? scaled_score(acc[r], scale_log2) : -INFINITY;
+                        } else {
+                            sv[c][j] = scaled_score(acc[r], scale_log2);
+                        }
+                    }
                 }
             }
-        }
-        // ---------------- max, weights, sum
-        float mx = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < kChunks; ++c)
+            for (int c = 0; c < kChunks; ++c)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) mx = fmaxf(mx, sv[c][j]);
-        mx = colmax_finish(mx);
-        bf16x8 pf[kChunks];
-        float ls = 0.0f;
+                for (int j = 0; j < 8; ++j) mx = fmaxf(mx, sv[c][j]);
+            mx = colmax_finish(mx);
 #pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-            float wv[8];
+            for (int c = 0; c < kChunks; ++c) {
+                float wv[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) wv[j] = weight_f32(sv[c][j], mx, (t0 + 32 * c + 8 * grp + j) <= pos);
-            pf[c] = pack_weights(wv);
-            ls = lsum_add(ls, pf[c]);
-        }
-        ls = lsum_finish(ls);
+                for (int j = 0; j < 8; ++j)
+                    wv[j] = weight_f32(sv[c][j], mx, kMasked ? (t0 + 32 * c + 8 * grp + j) <= pos : true);
+                pf[c] = pack_weights(wv);
+                ls = lsum_add(ls, pf[c]);
+            }
+            ls = lsum_finish(ls);
+        };
+        if (wave_full && t0 + kSplit - 1 <= wave_pos0)
+            softmax_part(std::false_type{});
+        else
+            softmax_part(std::true_type{});
         __syncthreads();                 // V of split i landed; every wave is done with s_k
         if (i + 1 < nsplit) issue_k(i + 1);
         // ---------------- values (dims past the sequence end are zeroed: stale LDS)
