@@ -204,22 +204,33 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
             softmax_part(std::true_type{});
         __syncthreads();                 // V of split i landed; every wave is done with s_k
         if (i + 1 < nsplit) issue_k(i + 1);
-        // ---------------- values (dims past the sequence end are zeroed: stale LDS)
+        // ---------------- values.  In the split that holds the sequence end, the
+        // value slots past it are stale LDS (possibly NaN) and are zeroed; every
+        // other split is whole.
         f32x4 o[8];
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto values_part = [&](auto tail) {
+            constexpr bool kTail = decltype(tail)::value;
 #pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-            const int tok = t0 + 32 * c + 8 * grp;
-            const int b = 2 * c + (grp >> 1);
+            for (int c = 0; c < kChunks; ++c) {
+                const int tok = t0 + 32 * c + 8 * grp;
+                const int b = 2 * c + (grp >> 1);
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const int d = 16 * dt + col;
-                u32x4 v = ld16(s_v + b * (kD * kBlock) + d * kBlock + vhalf(d, grp & 1) * 8);
-                if (tok + 8 > L) v = tok >= L ? zero_u32x4() : keep_first(v, L - tok);
-                o[dt] = pv_step(as_bf16x8(v), pf[c], o[dt]);
+                for (int dt = 0; dt < 8; ++dt) {
+                    const int d = 16 * dt + col;
+                    u32x4 v = ld16(s_v + b * (kD * kBlock) + d * kBlock + vhalf(d, grp & 1) * 8);
+                    if constexpr (kTail) {
+                        if (tok + 8 > L) v = tok >= L ? zero_u32x4() : keep_first(v, L - tok);
+                    }
+                    o[dt] = pv_step(as_bf16x8(v), pf[c], o[dt]);
+                }
             }
-        }
+        };
+        if (t0 + kSplit <= L)
+            values_part(std::false_type{});
+        else
+            values_part(std::true_type{});
         // ---------------- fold
         if (i == 0) {
             M = mx;
