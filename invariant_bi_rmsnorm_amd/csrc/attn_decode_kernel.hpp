@@ -110,6 +110,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         }
         __syncthreads();
 
+        // a split that ends before the sequence does needs no masking (the
+        // masked code gives the same values there, with more instructions)
+        const bool whole = t0 + kSplit <= L;
+
         // values operands of this wave's two head-dim tiles, all 8 chunks
         // (issued first: they do not depend on the scores)
         u32x4 vv[kChunks][2];
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
                 vv[c][dd] = zero_u32x4();
                 if (ok) {
                     vv[c][dd] = ld16(vc + (((int64_t)blk * Hkv + g) * kD + d) * kBlock + (tok & 15));
-                    if (tok + 8 > L) vv[c][dd] = keep_first(vv[c][dd], L - tok);
+                    if (!whole && tok + 8 > L) vv[c][dd] = keep_first(vv[c][dd], L - tok);
                 }
             }
         }
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = 4 * h + r;
-                    const bool valid = (t0 + 32 * c + 8 * grp + j) < L;
+                    const bool valid = whole || (t0 + 32 * c + 8 * grp + j) < L;
                     sv[cc][j] = valid ? scaled_score(acc[r], scale_log2) : -INFINITY;
                 }
             }
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
             float wv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                wv[j] = weight_f32(sv[cc][j], m, (t0 + 32 * c + 8 * grp + j) < L);
+                wv[j] = weight_f32(sv[cc][j], m, whole || (t0 + 32 * c + 8 * grp + j) < L);
             st16(&s_pt[col * kPtStride + 32 * c + 8 * grp], as_u32x4(pack_weights(wv)));
         }
         __syncthreads();
