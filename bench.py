@@ -376,7 +376,23 @@ def main():
                        + 4 * int(sum(-(-int(L) // 16) for L in ls)))
                 rows.append({"S": Sd, "kv_tokens": int(ls.sum()), "us": round(us, 2),
                              "GB/s": round(byt / (us * 1e-6) / 1e9, 1)})
+            # the same calls through the non-invariant build (split length chosen
+            # from the batch, as a load-tuned kernel would): what fixed splits cost
+            prev = ops.use_library(ops.NB_LIB_PATH)
+            try:
+                ws_nb = torch.empty(ops.bi_attention_workspace_bytes(S_DEC, I.ATT_HQ, I.ATT_D, max_len) // 4 + 4,
+                                    dtype=torch.float32, device=dev)
+                for r in rows:
+                    Sd = r["S"]
+                    ls = lens[:Sd]
+                    ml = int(ls.max())
+                    r["nb_us"] = round(graph_us(lambda: ops.bi_attention_decode(
+                        qd[:Sd], kc, vc, tbl[:Sd], lens_d[:Sd], ml, scale, ws=ws_nb, out=dec_out[:Sd]), 10), 2)
+            finally:
+                ops.use_library(prev)
+            del ws_nb
             extra["decode_S_sweep"] = {"rows": rows, "includes": "split + combine (no append)",
+                                       "nb_us": "libbi_nb.so: split length from the load (not invariant)",
                                        "note": "aggregate KV below the 256 MB MALL at small S"}
         if "prefill" not in skip:
             log("supplementary: prefill P sweep")
