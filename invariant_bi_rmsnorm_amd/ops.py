@@ -134,6 +134,20 @@ def _need(t: torch.Tensor, dtype, name: str):
         raise ValueError(f"{name} must be contiguous in its last dimension")
 
 
+def _need_shape(t: torch.Tensor, shape, name: str):
+    """Exact shape (None = any extent) and a dense layout: the C side sees only
+    the pointer and the sizes passed with it."""
+    if t.dim() != len(shape) or any(d is not None and t.shape[i] != d for i, d in enumerate(shape)):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_dense(t: torch.Tensor, dtype, shape, name: str):
+    _need(t, dtype, name)
+    _need_shape(t, shape, name)
+
+
 def _row_stride(t: torch.Tensor, row_extent: int) -> int:
     """Elements between consecutive rows; a one-row tensor may carry any stride
     (torch keeps 0 or odd strides on size-1 dimensions), so use the row extent."""
@@ -153,12 +167,18 @@ def abi_version() -> int:
 # ---------------------------------------------------------------------------
 def bi_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float, y: torch.Tensor = None,
                rstd: torch.Tensor = None, want_rstd: bool = True, stream=None):
-    _need(x, torch.bfloat16, "x"); _need(w, torch.bfloat16, "w")
+    _need(x, torch.bfloat16, "x")
     M, H = x.shape
+    _need_dense(w, torch.bfloat16, (H,), "w")
     if y is None:
         y = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    _need(y, torch.bfloat16, "y")
+    if tuple(y.shape) != (M, H):
+        raise ValueError(f"y must have shape {(M, H)}")
     if rstd is None and want_rstd:
         rstd = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if rstd is not None:
+        _need_dense(rstd, torch.float32, (M,), "rstd")
     _check(lib().bi_rmsnorm(_ptr(x), _ld(x), _ptr(w), _ptr(y), _ld(y), _ptr(rstd), M, H,
                             float(eps), _stream(stream)), "bi_rmsnorm")
     return y, rstd
@@ -177,6 +197,9 @@ def bi_matmul(a: torch.Tensor, wt: torch.Tensor, out_dtype=torch.bfloat16, c: to
     code = BI_BF16 if c.dtype == torch.bfloat16 else BI_F32 if c.dtype == torch.float32 else None
     if code is None:
         raise ValueError("c must be bfloat16 or float32")
+    _need(c, c.dtype, "c")
+    if tuple(c.shape) != (M, N):
+        raise ValueError(f"c must have shape {(M, N)}")
     _check(lib().bi_matmul(_ptr(a), _ld(a), _ptr(wt), _ld(wt), _ptr(c), _ld(c), code, M, N, K,
                            _stream(stream)), "bi_matmul")
     return c
@@ -193,8 +216,10 @@ def bi_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slots: torch.Tensor,
     ld = _row_stride(k_new, Hkv * D)
     if ld != _row_stride(v_new, Hkv * D):
         raise ValueError("k_new and v_new must share the row stride")
-    _need(slots, torch.int32, "slots")
+    _need_dense(slots, torch.int32, (T,), "slots")
     num_blocks = k_cache.shape[0]
+    _need_dense(k_cache, torch.bfloat16, (num_blocks, Hkv, 16, D), "k_cache")
+    _need_dense(v_cache, torch.bfloat16, (num_blocks, Hkv, D, 16), "v_cache")
     _check(lib().bi_kv_append(_ptr(k_new), _ptr(v_new), ld, _ptr(slots), T,
                               _ptr(k_cache), _ptr(v_cache), num_blocks, Hkv, D, _stream(stream)),
            "bi_kv_append")
@@ -215,6 +240,14 @@ def _heads_view(q: torch.Tensor, name: str):
     return H, D, _row_stride(q, H * D)
 
 
+def _check_paged(k_cache, v_cache, block_table, D):
+    nb, Hkv = k_cache.shape[0], k_cache.shape[1]
+    _need_dense(k_cache, torch.bfloat16, (nb, Hkv, 16, D), "k_cache")
+    _need_dense(v_cache, torch.bfloat16, (nb, Hkv, D, 16), "v_cache")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [S, max_blocks]")
+
+
 def bi_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                         block_table: torch.Tensor, kv_lens: torch.Tensor, max_kv_len: int,
                         scale: float, ws: torch.Tensor = None, out: torch.Tensor = None,
@@ -223,12 +256,19 @@ def bi_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
     S = q.shape[0]
     Hq, D, ldq = _heads_view(q, "q")
     Hkv = k_cache.shape[1]
+    _check_paged(k_cache, v_cache, block_table, D)
+    _need_dense(block_table, torch.int32, (S, None), "block_table")
+    _need_dense(kv_lens, torch.int32, (S,), "kv_lens")
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q.device)
     _, _, ldo = _heads_view(out, "out")
+    if tuple(out.shape) != (S, Hq, D):
+        raise ValueError(f"out must have shape {(S, Hq, D)}")
     need = bi_attention_workspace_bytes(S, Hq, D, max_kv_len)
     if ws is None:
         ws = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=q.device)
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous device tensor")
     _check(lib().bi_attention_decode(_ptr(q), ldq, _ptr(k_cache), _ptr(v_cache),
                                      k_cache.shape[0], _ptr(block_table), block_table.shape[1],
                                      _ptr(kv_lens), _ptr(out), ldo, S, Hq, Hkv, D,
@@ -246,10 +286,16 @@ def bi_attention_prefill(q: torch.Tensor, q_start: torch.Tensor, kv_lens: torch.
     T = q.shape[0]
     Hq, D, ldq = _heads_view(q, "q")
     Hkv = k_cache.shape[1]
+    _check_paged(k_cache, v_cache, block_table, D)
+    _need_dense(q_start, torch.int32, (None,), "q_start")
     S = q_start.shape[0] - 1
+    _need_dense(kv_lens, torch.int32, (S,), "kv_lens")
+    _need_dense(block_table, torch.int32, (S, None), "block_table")
     if out is None:
         out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=q.device)
     _, _, ldo = _heads_view(out, "out")
+    if tuple(out.shape) != (T, Hq, D):
+        raise ValueError(f"out must have shape {(T, Hq, D)}")
     _check(lib().bi_attention_prefill(_ptr(q), ldq, _ptr(q_start), _ptr(kv_lens),
                                       _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
                                       _ptr(block_table), block_table.shape[1], _ptr(out), ldo,
@@ -263,12 +309,16 @@ def bi_argmax(logits: torch.Tensor, ids: torch.Tensor = None, stream=None) -> to
     rows, V = logits.shape
     if ids is None:
         ids = torch.empty((rows,), dtype=torch.int32, device=logits.device)
+    _need_dense(ids, torch.int32, (rows,), "ids")
     _check(lib().bi_argmax(_ptr(logits), _ld(logits), rows, V, _ptr(ids), _stream(stream)),
            "bi_argmax")
     return ids
 
 
 def bi_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    for t, n in ((src, "src"), (dst, "dst")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous device tensor")
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst too small")
@@ -276,6 +326,8 @@ def bi_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
 
 
 def bi_probe_mfma_bf16(a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:
+    _need_dense(a, torch.bfloat16, (16, 32), "a")
+    _need_dense(b, torch.bfloat16, (32, 16), "b")
     c = torch.empty((16, 16), dtype=torch.float32, device=a.device)
     _check(lib().bi_probe_mfma_bf16(_ptr(a), _ptr(b), _ptr(c), _stream(stream)), "bi_probe_mfma_bf16")
     return c
@@ -286,8 +338,10 @@ def bi_probe_mfma_bf16(a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.T
 # ---------------------------------------------------------------------------
 
 def bi_embed(table: torch.Tensor, ids: torch.Tensor, out: torch.Tensor = None, stream=None):
-    _need(table, torch.bfloat16, "table"); _need(ids, torch.int32, "ids")
+    _need(table, torch.bfloat16, "table")
     V, H = table.shape
+    _need_shape(table, (V, H), "table")
+    _need_dense(ids, torch.int32, (None,), "ids")
     T = ids.shape[0]
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=table.device)
@@ -305,16 +359,19 @@ def bi_rope_table(max_pos: int, D: int, theta: float, stream=None) -> torch.Tens
 def bi_rope(x: torch.Tensor, pos: torch.Tensor, table: torch.Tensor, max_pos: int, stream=None):
     """In place on x [T, H, D] (rows may be strided)."""
     H, D, ld = _heads_view(x, "x")
-    _need(pos, torch.int32, "pos")
+    _need_dense(pos, torch.int32, (x.shape[0],), "pos")
+    _need_dense(table, torch.float32, (max_pos * D,), "table")
     _check(lib().bi_rope(_ptr(x), ld, H, D, _ptr(pos), x.shape[0], _ptr(table), max_pos,
                          _stream(stream)), "bi_rope")
     return x
 
 
 def bi_add(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor = None, stream=None):
-    _need(a, torch.bfloat16, "a"); _need(b, torch.bfloat16, "b")
+    _need_dense(a, torch.bfloat16, tuple(a.shape), "a")
+    _need_dense(b, torch.bfloat16, tuple(a.shape), "b")
     if out is None:
         out = torch.empty_like(a)
+    _need_dense(out, torch.bfloat16, tuple(a.shape), "out")
     _check(lib().bi_add(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)), "bi_add")
     return out
 

@@ -171,3 +171,19 @@ def test_toy_entry_validation(L):
     assert L.bi_gather_rows(A16, 64, 5, A16, 2, 64, A16, 60, None) == 1    # ldd < W
     assert L.bi_toy_workspace_bytes(None, 10, 2, 100) == 0
     assert L.bi_toy_step(None, None, None, None, 0, None, None, None) == 1
+
+
+def test_binding_shape_checks():
+    """The binding refuses tensors whose shape, dtype or layout disagrees with
+    what it passes to the C side (the library sees only pointers and sizes)."""
+    import torch
+    from invariant_bi_rmsnorm_amd import ops
+    ops._need_shape(torch.zeros(2, 3), (2, None), "x")
+    with pytest.raises(ValueError):
+        ops._need_shape(torch.zeros(2, 3), (3, None), "x")
+    with pytest.raises(ValueError):
+        ops._need_shape(torch.zeros(2, 3), (2, 3, 1), "x")
+    with pytest.raises(ValueError):
+        ops._need_shape(torch.zeros(3, 2).t(), (2, 3), "x")           # not contiguous
+    with pytest.raises(ValueError):
+        ops._need(torch.zeros(2, 3, dtype=torch.bfloat16), torch.bfloat16, "x")   # host tensor
