@@ -55,6 +55,7 @@ def _load():
     lib.or_matmul_f64.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64]
     lib.or_attention.argtypes = [P, I64, P, P, P, I64, I32, I32, I32, D, P, P, P]
     lib.or_argmax.argtypes = [P, I64, I64, I64, P]
+    lib.or_log_softmax.argtypes = [P, I64, P, I64, I64, I64]
     lib.or_num_threads.restype = ctypes.c_int
     lib.or_rope.argtypes = [P, P, P, I64, I32, I32, D]
     lib.or_silu_mul.argtypes = [P, P, P, I64]
@@ -230,6 +231,15 @@ def add(a, b):
     out = np.empty_like(a)
     _load().or_add(_p(a), _p(b), _p(out), a.size)
     return out
+
+
+def log_softmax(x, ld=None):
+    """x [rows, V] float32 -> log_softmax over the last dimension, float64 [rows, V]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, V = x.shape
+    y = np.empty((rows, V), dtype=np.float64)
+    _load().or_log_softmax(_p(x), V, _p(y), V, rows, V)
+    return y
 
 
 class _ToyCfg(ctypes.Structure):

@@ -265,6 +265,36 @@ void or_argmax(const float* logits, int64_t ld, int64_t rows, int64_t V, int32_t
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* log_softmax over the last dimension.  The page post "論文／ブログ          */
+/* 「Defeating Nondeterminism in LLM Inference」の技術的なポイント", section     */
+/* 他の演算子（RMSNorm, MatMul, mean/reduction etc.）, lists log_softmax among */
+/* the reductions the invariant library replaces; the op itself is the usual */
+/* one, written out:                                                         */
+/*     y_i = x_i - m - log( sum_j exp(x_j - m) ),  m = max_j x_j             */
+/* in double precision.  A row whose maximum is -inf (every entry -inf) or   */
+/* +inf, or that holds a NaN, gives NaN where the formula does.              */
+/* ------------------------------------------------------------------------ */
+
+void or_log_softmax(const float* x, int64_t ldx, double* y, int64_t ldy, int64_t rows, int64_t V)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * ldx;
+        double m = -INFINITY;
+        int has_nan = 0;
+        for (int64_t i = 0; i < V; ++i) {
+            if (isnan(xr[i])) has_nan = 1;
+            else if ((double)xr[i] > m) m = (double)xr[i];
+        }
+        double s = 0.0;
+        for (int64_t i = 0; i < V; ++i) s += exp((double)xr[i] - m);
+        const double lse = m + log(s);
+        for (int64_t i = 0; i < V; ++i)
+            y[r * ldy + i] = has_nan ? NAN : (double)xr[i] - lse;
+    }
+}
+
 int or_num_threads(void)
 {
 #if defined(_OPENMP)

@@ -29,6 +29,9 @@ MUTANTS = {
     "silu_wrong_sign": ("gv / (1.0 + exp(-gv))", "gv / (1.0 + exp(gv))"),
     "add_subtracts": ("bf16_bits_to_double(a[i]) + bf16_bits_to_double(b[i])",
                       "bf16_bits_to_double(a[i]) - bf16_bits_to_double(b[i])"),
+    "log_softmax_drops_max": ("const double lse = m + log(s);", "const double lse = log(s);"),
+    "log_softmax_drops_first_term": ("for (int64_t i = 0; i < V; ++i) s += exp", "for (int64_t i = 1; i < V; ++i) s += exp"),
+    "log_softmax_wrong_sign": ("(double)xr[i] - lse;", "lse - (double)xr[i];"),
     "toy_no_final_norm": ("or_rmsnorm(h + (T - 1) * H, H, final_norm, xn, H, NULL, 1, H, c->eps);",
                           "memcpy(xn, h + (T - 1) * H, (size_t)H * 2);"),
     "toy_value_from_key_slot": ("memcpy(vv + t * Hkv * D, qkv + t * QKV + (Hq + Hkv) * D",

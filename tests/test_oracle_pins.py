@@ -349,6 +349,73 @@ def test_argmax_ties_lowest_index_and_nan(orc):
     assert orc.argmax(x[7:8])[0] == -1
 
 
+# ---------------------------------------------------------------- log_softmax
+
+def test_log_softmax_uniform_row_is_minus_log_V(orc):
+    for V in (1, 2, 7, 32000):
+        x = np.full((2, V), 3.25, np.float32)
+        x[1] = -11.0
+        y = orc.log_softmax(x)
+        assert np.allclose(y, -math.log(V), rtol=0, atol=1e-12)
+
+
+def test_log_softmax_two_entries_closed_form(orc):
+    g = np.random.default_rng(40)
+    x = g.uniform(-20, 20, (30, 2)).astype(np.float32)
+    y = orc.log_softmax(x)
+    for r in range(30):
+        a, b = float(x[r, 0]), float(x[r, 1])
+        assert abs(y[r, 0] + math.log1p(math.exp(b - a))) < 1e-12
+        assert abs(y[r, 1] + math.log1p(math.exp(a - b))) < 1e-12
+
+
+def test_log_softmax_one_large_entry_closed_form(orc):
+    V = 1000
+    for a in (0.5, 7.0, 40.0):
+        x = np.zeros((1, V), np.float32)
+        x[0, 3] = a
+        y = orc.log_softmax(x)[0]
+        z = math.exp(a) + (V - 1)
+        assert abs(y[3] - (a - math.log(z))) < 1e-12
+        assert np.allclose(np.delete(y, 3), -math.log(z), rtol=0, atol=1e-12)
+
+
+def test_log_softmax_shift_invariance_and_normalisation(orc):
+    g = np.random.default_rng(41)
+    x = np.round(g.standard_normal((20, 500)) * 4).astype(np.float32)     # integers: x + c exact
+    y = orc.log_softmax(x)
+    y2 = orc.log_softmax(x + np.float32(1000.0))                            # exp(1000) overflows unshifted
+    assert np.allclose(y, y2, rtol=0, atol=1e-10)
+    assert np.allclose(np.exp(y).sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(np.argmax(y, axis=1) == np.argmax(x, axis=1))
+
+
+def test_log_softmax_brute_force_decimal(orc):
+    g = np.random.default_rng(42)
+    x = (g.integers(-300, 300, (6, 7)) / 16).astype(np.float32)           # exact in float32
+    y = orc.log_softmax(x)
+    with decimal.localcontext(CTX):
+        for r in range(6):
+            s = sum(dec(float(v)).exp() for v in x[r])
+            lse = s.ln()
+            for i in range(7):
+                assert abs(float(dec(float(x[r, i])) - lse) - y[r, i]) < 1e-12
+
+
+def test_log_softmax_masked_entries_and_nan(orc):
+    g = np.random.default_rng(43)
+    x = g.standard_normal((3, 64)).astype(np.float32)
+    x[0, ::3] = -np.inf                                   # masked logits
+    y = orc.log_softmax(x)
+    keep = np.isfinite(x[0])
+    assert np.all(y[0, ~keep] == -np.inf)
+    assert np.allclose(y[0, keep], orc.log_softmax(x[0:1, keep])[0], rtol=0, atol=1e-12)
+    x[1] = -np.inf                                        # nothing left to normalise over
+    x[2, 5] = np.nan
+    y = orc.log_softmax(x)
+    assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[2]))
+
+
 # ---------------------------------------------------------------- sanity
 
 def test_float_addition_order_matters():
