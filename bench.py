@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--skip", default="", help="comma list of phases to skip: decode,prefill")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the supplementary points (RMSNorm 1 GiB, decode S sweep, prefill P sweep)")
+                    help="skip the supplementary points (RMSNorm 1 GiB, log_softmax, decode S sweep, prefill P sweep)")
     return ap.parse_args()
 
 
@@ -364,6 +364,17 @@ def main():
                                        "GB/s": round(byt / (us * 1e-6) / 1e9, 1),
                                        "frac_hbm": round(byt / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         del xb, yb
+        log("supplementary: log_softmax")
+        for rows_ls in (256, 8192):
+            Vls = 32000
+            xl = torch.randn((rows_ls, Vls), device=dev, dtype=torch.float32) * 3
+            yl = torch.empty_like(xl)
+            us = graph_us(lambda: ops.bi_log_softmax(xl, out=yl), 5)
+            byt = 8 * rows_ls * Vls
+            extra[f"log_softmax_{rows_ls}x{Vls}"] = {"us": round(us, 1), "bytes": byt,
+                                                    "GB/s": round(byt / (us * 1e-6) / 1e9, 1),
+                                                    "frac_hbm": round(byt / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            del xl, yl
         if "decode" not in skip:
             log("supplementary: decode S sweep")
             rows = []

@@ -173,6 +173,25 @@ int bi_attention_prefill(const void* q, int64_t ldq, const int32_t* q_start,
                          void* stream);
 
 /*
+ * log_softmax over the last dimension, batch-invariant (post "論文／ブログ
+ * 「Defeating Nondeterminism in LLM Inference」の技術的なポイント", section
+ * 他の演算子（RMSNorm, MatMul, mean/reduction etc.）: log_softmax is one of the
+ * reductions the invariant library replaces).  For every row r:
+ *     y[r][i] = x[r][i] - m - log(sum_j exp(x[r][j] - m)),  m = max_j x[r][j]
+ * with one reduction order that depends only on V (one row per workgroup;
+ * see csrc/log_softmax.hip), so a row's bits do not depend on rows, on the
+ * row's position or on the other rows.
+ *
+ * x [rows][ldx] fp32, y [rows][ldy] fp32, device pointers, 4-byte aligned;
+ * ldx, ldy >= V; in place (x == y) only with ldx == ldy.  A row holding a NaN
+ * becomes all NaN; a row whose maximum is -inf (all -inf) or +inf becomes NaN
+ * where the formula gives NaN; -inf entries of other rows give -inf.
+ * rows == 0 is a no-op; rows and V up to 2^31 - 513.
+ */
+int bi_log_softmax(const float* x, int64_t ldx, float* y, int64_t ldy, int64_t rows, int64_t V,
+                   void* stream);
+
+/*
  * Greedy token choice (temperature 0 = argmax at every step; page
  * "la température zéro n'est pas déterministe", section "Le mensonge de la
  * température zéro").  ids[r] = index of the largest logit of row r, ties to

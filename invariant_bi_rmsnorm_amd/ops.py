@@ -49,6 +49,7 @@ SIGNATURES = {
     "bi_attention_prefill": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _P, _I32, _P, _I64,
                                             _I32, _I64, _I32, _I32, _I32, _I32, _F, _P]),
     "bi_argmax": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
+    "bi_log_softmax": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P]),
     "bi_probe_mfma_bf16": (ctypes.c_int, [_P, _P, _P, _P]),
     "bi_probe_copy": (ctypes.c_int, [_P, _P, _I64, _P]),
     # include/bi_toy.h
@@ -313,6 +314,20 @@ def bi_argmax(logits: torch.Tensor, ids: torch.Tensor = None, stream=None) -> to
     _check(lib().bi_argmax(_ptr(logits), _ld(logits), rows, V, _ptr(ids), _stream(stream)),
            "bi_argmax")
     return ids
+
+
+def bi_log_softmax(x: torch.Tensor, out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """log_softmax over the last dimension of x [rows, V] (fp32); out may be x."""
+    _need(x, torch.float32, "x")
+    rows, V = x.shape
+    if out is None:
+        out = torch.empty((rows, V), dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, "out")
+    if tuple(out.shape) != (rows, V):
+        raise ValueError(f"out must have shape {(rows, V)}")
+    _check(lib().bi_log_softmax(_ptr(x), _ld(x), _ptr(out), _ld(out), rows, V, _stream(stream)),
+           "bi_log_softmax")
+    return out
 
 
 def bi_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):

@@ -187,3 +187,14 @@ def test_binding_shape_checks():
         ops._need_shape(torch.zeros(3, 2).t(), (2, 3), "x")           # not contiguous
     with pytest.raises(ValueError):
         ops._need(torch.zeros(2, 3, dtype=torch.bfloat16), torch.bfloat16, "x")   # host tensor
+
+
+def test_log_softmax_validation(L):
+    f = L.bi_log_softmax
+    assert f(A16, 100, A16, 100, 0, 100, None) == 0            # rows == 0 no-op
+    assert f(A16, 99, A16, 100, 4, 100, None) == 1             # ldx < V
+    assert f(A16, 100, A16, 99, 4, 100, None) == 1             # ldy < V
+    assert f(A16, 100, A16, 100, 4, 0, None) == 1              # V == 0
+    assert f(None, 100, A16, 100, 4, 100, None) == 1           # null x
+    assert f(A16 + 2, 100, A16, 100, 4, 100, None) == 1        # misaligned
+    assert f(A16, 100, A16, 128, 4, 100, None) == 1            # in place with different ld

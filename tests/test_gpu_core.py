@@ -260,3 +260,58 @@ def test_bf16_rounding_edges(ops, orc):
     n[1] = 0xFF81
     out = host_bits(ops.bi_add(dev_bf16(n), dev_bf16(np.full(8, 0x3F80, np.uint16))))
     assert all((int(v) & 0x7F80) == 0x7F80 and (int(v) & 0x7F) != 0 for v in out[:2])
+
+
+# ------------------------------------------------------------------ log_softmax
+
+def _check_log_softmax(got, ref, x, what):
+    # fp32 arithmetic.  log(sum): per-term exp error (a few ulp) and a 63-term
+    # sequential sum per thread plus a 9-level tree keep its error below 1e-5.
+    # lse = m + log(sum) and y = x - lse each round at the magnitude of x and
+    # lse (half an ulp = 2^-24 of it; x - m and x - lse are exact when close).
+    # Bar: 2e-5 + 2^-23 (|x| + |lse|), lse taken from the exact result.
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), what
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), what
+    err = np.abs(got[fin].astype(np.float64) - ref[fin])
+    xf = x[fin].astype(np.float64)
+    bound = 2e-5 + 2.0 ** -23 * (np.abs(xf) + np.abs(xf - ref[fin]))
+    assert np.all(err <= bound), f"{what}: max err {err.max():.3e}"
+    return float(err.max()) if err.size else 0.0
+
+
+@pytest.mark.parametrize("V", [1, 7, 511, 513, 1000, 32000, 32768, 32769, 70001])
+def test_log_softmax_parity(ops, orc, V):
+    g = np.random.default_rng(V)
+    rows = 37 if V <= 32768 else 5
+    x = (g.standard_normal((rows, V)) * 3).astype(np.float32)
+    x[1] += np.float32(1000.0)                        # large logits: needs the max shift
+    if V > 4:
+        x[2, ::4] = -np.inf                           # masked entries
+    x[3] = -np.inf                                    # nothing to normalise over -> NaN row
+    x[4, V // 2] = np.nan                             # NaN row
+    got = ops.bi_log_softmax(torch.from_numpy(x).cuda()).cpu().numpy()
+    e = _check_log_softmax(got, orc.log_softmax(x), x, f"log_softmax V={V}")
+    log(f"log_softmax V={V}: max |err| {e:.2e}")
+
+
+def test_log_softmax_batch_invariance_and_in_place(ops):
+    g = np.random.default_rng(77)
+    V = 32000
+    row = (g.standard_normal(V) * 4).astype(np.float32)
+    alone = ops.bi_log_softmax(torch.from_numpy(row[None].copy()).cuda()).cpu().numpy()[0]
+    for B in (2, 3, 8, 64, 257):
+        x = (g.standard_normal((B, V)) * 4).astype(np.float32)
+        p = int(g.integers(0, B))
+        x[p] = row
+        got = ops.bi_log_softmax(torch.from_numpy(x).cuda()).cpu().numpy()
+        assert np.array_equal(got[p].view(np.uint32), alone.view(np.uint32)), f"B={B} p={p}"
+    xd = torch.from_numpy(np.stack([row, row])).cuda()
+    ops.bi_log_softmax(xd, out=xd)                    # in place
+    assert np.array_equal(xd.cpu().numpy()[1].view(np.uint32), alone.view(np.uint32))
+    # a row inside a wider allocation (ld > V)
+    wide = torch.zeros((3, V + 64), dtype=torch.float32, device="cuda")
+    wide[1, :V] = torch.from_numpy(row).cuda()
+    out = torch.zeros((3, V + 96), dtype=torch.float32, device="cuda")
+    ops.bi_log_softmax(wide[:, :V], out=out[:, :V])
+    assert np.array_equal(out[1, :V].cpu().numpy().view(np.uint32), alone.view(np.uint32))
