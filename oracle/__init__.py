@@ -56,6 +56,8 @@ def _load():
     lib.or_attention.argtypes = [P, I64, P, P, P, I64, I32, I32, I32, D, P, P, P]
     lib.or_argmax.argtypes = [P, I64, I64, I64, P]
     lib.or_log_softmax.argtypes = [P, I64, P, I64, I64, I64]
+    lib.or_philox4x32_10.argtypes = [P, P, P, I64]
+    lib.or_sample.argtypes = [P, I64, I64, I64, ctypes.c_float, P, P, P, P]
     lib.or_num_threads.restype = ctypes.c_int
     lib.or_rope.argtypes = [P, P, P, I64, I32, I32, D]
     lib.or_silu_mul.argtypes = [P, P, P, I64]
@@ -240,6 +242,29 @@ def log_softmax(x, ld=None):
     y = np.empty((rows, V), dtype=np.float64)
     _load().or_log_softmax(_p(x), V, _p(y), V, rows, V)
     return y
+
+
+def philox4x32_10(ctr, key):
+    """ctr [n, 4] uint32, key [n, 2] uint32 -> [n, 4] uint32 (Philox4x32-10)."""
+    ctr = np.ascontiguousarray(ctr, dtype=np.uint32).reshape(-1, 4)
+    key = np.ascontiguousarray(key, dtype=np.uint32).reshape(-1, 2)
+    out = np.empty_like(ctr)
+    _load().or_philox4x32_10(_p(ctr), _p(key), _p(out), ctr.shape[0])
+    return out
+
+
+def sample(x, temperature: float, seeds, offsets, with_scores: bool = False):
+    """Gumbel-max sampling of each row of x [rows, V] float32 at temperature > 0.
+    Returns ids int32 [rows] (and the float64 scores [rows, V] if asked)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, V = x.shape
+    seeds = np.ascontiguousarray(seeds, dtype=np.uint64)
+    offsets = np.ascontiguousarray(offsets, dtype=np.uint64)
+    ids = np.empty(rows, dtype=np.int32)
+    sc = np.empty((rows, V), dtype=np.float64) if with_scores else None
+    _load().or_sample(_p(x), V, rows, V, float(np.float32(temperature)), _p(seeds), _p(offsets),
+                      _p(ids), _p(sc) if sc is not None else None)
+    return (ids, sc) if with_scores else ids
 
 
 class _ToyCfg(ctypes.Structure):

@@ -295,6 +295,75 @@ void or_log_softmax(const float* x, int64_t ldx, double* y, int64_t ldy, int64_t
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Seeded sampling at temperature T > 0 (extends the greedy experiment of    */
+/* the page "la température zéro n'est pas déterministe" to sampled          */
+/* decoding): the Gumbel-max rule                                            */
+/*     id = argmax_i ( x_i / T + g_i ),   g_i = -log(-log(u_i))               */
+/* picks i with probability softmax(x / T)_i.  The uniforms come from the    */
+/* counter-based generator Philox4x32-10 (Salmon, Moraes, Dror, Shaw,        */
+/* "Parallel random numbers: as easy as 1, 2, 3", SC 2011): key = the row's */
+/* 64-bit seed, counter = (i, offset low, offset high, 0), first output word */
+/*     u_i = ((word >> 8) + 0.5) * 2^-24   in (0, 1).                        */
+/* Everything after the 32-bit word is double precision.  Ties go to the     */
+/* lowest index; a NaN logit gives -1.                                       */
+/* ------------------------------------------------------------------------ */
+
+static void philox4x32_10(uint32_t ctr[4], uint32_t k0, uint32_t k1)
+{
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;   /* round multipliers   */
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;   /* key schedule (Weyl) */
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)M0 * ctr[0];
+        const uint64_t p1 = (uint64_t)M1 * ctr[2];
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        const uint32_t n0 = hi1 ^ ctr[1] ^ k0;
+        const uint32_t n2 = hi0 ^ ctr[3] ^ k1;
+        ctr[0] = n0;
+        ctr[1] = lo1;
+        ctr[2] = n2;
+        ctr[3] = lo0;
+        k0 += W0;
+        k1 += W1;
+    }
+}
+
+void or_philox4x32_10(const uint32_t* ctr_in, const uint32_t* key, uint32_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t c[4] = {ctr_in[4 * i], ctr_in[4 * i + 1], ctr_in[4 * i + 2], ctr_in[4 * i + 3]};
+        philox4x32_10(c, key[2 * i], key[2 * i + 1]);
+        for (int j = 0; j < 4; ++j) out[4 * i + j] = c[j];
+    }
+}
+
+static double gumbel_of(uint64_t seed, uint64_t offset, uint32_t i)
+{
+    uint32_t c[4] = {i, (uint32_t)offset, (uint32_t)(offset >> 32), 0u};
+    philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+    const double u = ((double)(c[0] >> 8) + 0.5) * 0x1p-24;
+    return -log(-log(u));
+}
+
+void or_sample(const float* logits, int64_t ld, int64_t rows, int64_t V, float temperature,
+               const uint64_t* seeds, const uint64_t* offsets, int32_t* ids, double* scores)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* x = logits + r * ld;
+        int32_t best = -1;
+        double bv = 0.0;
+        for (int64_t i = 0; i < V; ++i) {
+            if (isnan(x[i])) { best = -1; break; }
+            const double sc = (double)x[i] / (double)temperature + gumbel_of(seeds[r], offsets[r], (uint32_t)i);
+            if (scores) scores[r * V + i] = sc;
+            if (best < 0 || sc > bv) { best = (int32_t)i; bv = sc; }
+        }
+        ids[r] = best;
+    }
+}
+
 int or_num_threads(void)
 {
 #if defined(_OPENMP)

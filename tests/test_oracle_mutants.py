@@ -32,6 +32,9 @@ MUTANTS = {
     "log_softmax_drops_max": ("const double lse = m + log(s);", "const double lse = log(s);"),
     "log_softmax_drops_first_term": ("for (int64_t i = 0; i < V; ++i) s += exp", "for (int64_t i = 1; i < V; ++i) s += exp"),
     "log_softmax_wrong_sign": ("(double)xr[i] - lse;", "lse - (double)xr[i];"),
+    "philox_nine_rounds": ("for (int r = 0; r < 10; ++r) {", "for (int r = 0; r < 9; ++r) {"),
+    "gumbel_wrong_sign": ("return -log(-log(u));", "return log(-log(u));"),
+    "sample_multiplies_by_temperature": ("(double)x[i] / (double)temperature", "(double)x[i] * (double)temperature"),
     "toy_no_final_norm": ("or_rmsnorm(h + (T - 1) * H, H, final_norm, xn, H, NULL, 1, H, c->eps);",
                           "memcpy(xn, h + (T - 1) * H, (size_t)H * 2);"),
     "toy_value_from_key_slot": ("memcpy(vv + t * Hkv * D, qkv + t * QKV + (Hq + Hkv) * D",

@@ -416,6 +416,59 @@ def test_log_softmax_masked_entries_and_nan(orc):
     assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[2]))
 
 
+# ---------------------------------------------------------------- seeded sampling
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_philox_known_answer_vectors(orc):
+    rows = []
+    for line in open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")):
+        if line.strip() and not line.startswith("#"):
+            c, k, o = (np.array([int(w, 16) for w in part.split()], np.uint64) for part in line.split("|"))
+            rows.append((c, k, o))
+    assert len(rows) == 3
+    for c, k, o in rows:
+        assert np.array_equal(orc.philox4x32_10(c[None].astype(np.uint32), k[None].astype(np.uint32))[0],
+                              o.astype(np.uint32))
+
+
+def _chi2(counts, p):
+    n = counts.sum()
+    return float(((counts - n * p) ** 2 / (n * p)).sum())
+
+
+def test_sample_frequencies_follow_softmax_over_temperature(orc):
+    # Gumbel-max picks i with probability softmax(x / T)_i; 60000 seeded draws
+    # per case, chi-square with 3 degrees of freedom against 16.27 (p = 0.001)
+    x = np.array([[0.0, 1.0, 2.0, 3.0]], np.float32)
+    for T in (1.0, 0.5, 2.0):
+        n = 60000
+        ids = orc.sample(np.repeat(x, n, axis=0), T, np.arange(n, dtype=np.uint64) * 7919 + 3,
+                         np.full(n, 5, np.uint64))
+        counts = np.bincount(ids, minlength=4).astype(np.float64)
+        p = np.exp(x[0] / T) / np.exp(x[0] / T).sum()
+        assert _chi2(counts, p) < 16.27, (T, counts, p)
+
+
+def test_sample_small_temperature_is_argmax_and_draws_are_reproducible(orc):
+    g = np.random.default_rng(44)
+    x = np.round(g.standard_normal((40, 300)) * 8).astype(np.float32)
+    x += np.arange(300, dtype=np.float32)[None] * 1e-3               # no exact ties
+    seeds = g.integers(0, 2 ** 63, 40).astype(np.uint64)
+    offs = g.integers(0, 2 ** 40, 40).astype(np.uint64)
+    assert np.array_equal(orc.sample(x, 1e-4, seeds, offs), orc.argmax(x))
+    a = orc.sample(x, 1.0, seeds, offs)
+    assert np.array_equal(a, orc.sample(x, 1.0, seeds, offs))        # same key and counter, same draw
+    assert not np.array_equal(a, orc.sample(x, 1.0, seeds, offs + 1))  # another counter, another draw
+    # equal logits: the choice is the largest noise, so it moves with the seed
+    u = orc.sample(np.zeros((200, 50), np.float32), 1.0, np.arange(200, dtype=np.uint64),
+                   np.zeros(200, np.uint64))
+    assert len(set(u.tolist())) > 30
+    x[3, 17] = np.nan
+    assert orc.sample(x[3:4], 1.0, seeds[3:4], offs[3:4])[0] == -1
+
+
 # ---------------------------------------------------------------- sanity
 
 def test_float_addition_order_matters():
