@@ -192,6 +192,25 @@ int bi_log_softmax(const float* x, int64_t ldx, float* y, int64_t ldy, int64_t r
                    void* stream);
 
 /*
+ * Seeded sampling at temperature T > 0, batch-invariant: extends the greedy
+ * choice below (page "la température zéro n'est pas déterministe", section
+ * "Le mensonge de la température zéro") to sampled decoding.  Gumbel-max:
+ *     ids[r] = argmax_i ( x[r][i] / T + g_i ),  g_i = -log(-log(u_i)),
+ *     u_i = ((w_i >> 8) + 0.5) * 2^-24,
+ * w_i = first output word of Philox4x32-10 (Salmon et al., SC 2011) with key
+ * = seeds[r] (low word first) and counter = (i, offsets[r] low, offsets[r]
+ * high, 0); the division, logs and sum in double precision; ties to the lower
+ * index; -1 if the row holds a NaN.  This draws i with probability
+ * softmax(x[r] / T)_i, and a row's draw depends only on its logits, seed,
+ * offset and T.  Use a fresh offset (e.g. the token's position) per draw.
+ *
+ * logits [rows][ld] fp32; seeds, offsets [rows] uint64; ids [rows] int32;
+ * device pointers.  T must be finite and > 0 (T = 0 is bi_argmax).
+ */
+int bi_sample(const float* logits, int64_t ld, int64_t rows, int64_t V, float temperature,
+              const uint64_t* seeds, const uint64_t* offsets, int32_t* ids, void* stream);
+
+/*
  * Greedy token choice (temperature 0 = argmax at every step; page
  * "la température zéro n'est pas déterministe", section "Le mensonge de la
  * température zéro").  ids[r] = index of the largest logit of row r, ties to

@@ -50,6 +50,7 @@ SIGNATURES = {
                                             _I32, _I64, _I32, _I32, _I32, _I32, _F, _P]),
     "bi_argmax": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
     "bi_log_softmax": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P]),
+    "bi_sample": (ctypes.c_int, [_P, _I64, _I64, _I64, _F, _P, _P, _P, _P]),
     "bi_probe_mfma_bf16": (ctypes.c_int, [_P, _P, _P, _P]),
     "bi_probe_copy": (ctypes.c_int, [_P, _P, _I64, _P]),
     # include/bi_toy.h
@@ -328,6 +329,22 @@ def bi_log_softmax(x: torch.Tensor, out: torch.Tensor = None, stream=None) -> to
     _check(lib().bi_log_softmax(_ptr(x), _ld(x), _ptr(out), _ld(out), rows, V, _stream(stream)),
            "bi_log_softmax")
     return out
+
+
+def bi_sample(logits: torch.Tensor, temperature: float, seeds: torch.Tensor, offsets: torch.Tensor,
+              ids: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """Seeded Gumbel-max sampling of each row of logits [rows, V] (fp32) at
+    temperature > 0; seeds and offsets are uint64 [rows] (torch.int64 storage)."""
+    _need(logits, torch.float32, "logits")
+    rows, V = logits.shape
+    _need_dense(seeds, torch.int64, (rows,), "seeds")
+    _need_dense(offsets, torch.int64, (rows,), "offsets")
+    if ids is None:
+        ids = torch.empty((rows,), dtype=torch.int32, device=logits.device)
+    _need_dense(ids, torch.int32, (rows,), "ids")
+    _check(lib().bi_sample(_ptr(logits), _ld(logits), rows, V, float(temperature), _ptr(seeds),
+                           _ptr(offsets), _ptr(ids), _stream(stream)), "bi_sample")
+    return ids
 
 
 def bi_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):

@@ -198,3 +198,15 @@ def test_log_softmax_validation(L):
     assert f(None, 100, A16, 100, 4, 100, None) == 1           # null x
     assert f(A16 + 2, 100, A16, 100, 4, 100, None) == 1        # misaligned
     assert f(A16, 100, A16, 128, 4, 100, None) == 1            # in place with different ld
+
+
+def test_sample_validation(L):
+    f = L.bi_sample
+    assert f(A16, 100, 0, 100, 1.0, A16, A16, A16, None) == 0          # rows == 0
+    assert f(A16, 99, 2, 100, 1.0, A16, A16, A16, None) == 1           # ld < V
+    assert f(A16, 100, 2, 100, 0.0, A16, A16, A16, None) == 1          # T == 0 (use argmax)
+    assert f(A16, 100, 2, 100, -1.0, A16, A16, A16, None) == 1
+    assert f(A16, 100, 2, 100, float("inf"), A16, A16, A16, None) == 1
+    assert f(A16, 100, 2, 100, float("nan"), A16, A16, A16, None) == 1
+    assert f(A16, 100, 2, 100, 1.0, None, A16, A16, None) == 1         # null seeds
+    assert f(A16, 100, 2, 100, 1.0, A16 + 4, A16, A16, None) == 1      # misaligned seeds

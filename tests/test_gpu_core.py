@@ -315,3 +315,46 @@ def test_log_softmax_batch_invariance_and_in_place(ops):
     out = torch.zeros((3, V + 96), dtype=torch.float32, device="cuda")
     ops.bi_log_softmax(wide[:, :V], out=out[:, :V])
     assert np.array_equal(out[1, :V].cpu().numpy().view(np.uint32), alone.view(np.uint32))
+
+
+# ------------------------------------------------------------------ seeded sampling
+
+def _u64(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.uint64).view(np.int64)).cuda()
+
+
+@pytest.mark.parametrize("V,T", [(7, 1.0), (1000, 0.7), (32000, 1.0), (32000, 0.25), (70001, 2.0)])
+def test_sample_matches_oracle(ops, orc, V, T):
+    """The GPU draws the same ids as the oracle (same Philox words, the scores
+    in double on both sides); ties of two double scores, which could split
+    the two log implementations, do not occur at these sizes."""
+    g = np.random.default_rng(V + int(T * 100))
+    rows = 64
+    x = (g.standard_normal((rows, V)) * 2).astype(np.float32)
+    x[5] = 0.0                                         # flat row: the noise decides
+    x[6, ::3] = -np.inf
+    if V > 9:
+        x[7, 9] = np.nan
+    seeds = g.integers(0, 2 ** 64, rows, dtype=np.uint64)
+    offs = g.integers(0, 2 ** 64, rows, dtype=np.uint64)
+    got = ops.bi_sample(torch.from_numpy(x).cuda(), T, _u64(seeds), _u64(offs)).cpu().numpy()
+    ref = orc.sample(x, T, seeds, offs)
+    assert np.array_equal(got, ref)
+    if V > 9:
+        assert got[7] == -1
+
+
+def test_sample_batch_invariance(ops):
+    g = np.random.default_rng(78)
+    V = 32000
+    row = (g.standard_normal(V) * 2).astype(np.float32)
+    seed, off = np.uint64(0x1234_5678_9ABC_DEF0), np.uint64(77)
+    alone = ops.bi_sample(torch.from_numpy(row[None].copy()).cuda(), 0.8, _u64([seed]), _u64([off])).item()
+    for B in (2, 5, 64, 300):
+        x = (g.standard_normal((B, V)) * 2).astype(np.float32)
+        seeds = g.integers(0, 2 ** 64, B, dtype=np.uint64)
+        offs = g.integers(0, 2 ** 64, B, dtype=np.uint64)
+        p = int(g.integers(0, B))
+        x[p], seeds[p], offs[p] = row, seed, off
+        got = ops.bi_sample(torch.from_numpy(x).cuda(), 0.8, _u64(seeds), _u64(offs)).cpu().numpy()
+        assert got[p] == alone, f"B={B} p={p}"
