@@ -61,6 +61,7 @@ class Request:
     prompt: np.ndarray
     max_new: int
     target: bool = False
+    seed: int = 0                         # sampling key (T > 0); targets share one
     length: int = 0                       # tokens already in the cache
     pending: list = field(default_factory=list)
     generated: list = field(default_factory=list)
@@ -115,6 +116,7 @@ class ToyEngine:
         self.ws = torch.empty((nbytes,), dtype=torch.uint8, device=device)
         self.next_ids = torch.empty((max_seqs,), dtype=torch.int32, device=device)
         self.logits = torch.empty((max_seqs, cfg["vocab"]), dtype=torch.float32, device=device)
+        self.sampled = torch.empty((max_seqs,), dtype=torch.int32, device=device)
         self.free = list(range(num_blocks))[::-1]
         self.num_blocks = num_blocks
 
@@ -131,10 +133,12 @@ class ToyEngine:
         r.blocks = []
 
     # ---------------------------------------------------------------- one step
-    def step(self, work, want_logits: bool = False):
+    def step(self, work, want_logits: bool = False, temperature: float = 0.0):
         """work: list of (request, n_tokens) with all decode entries (n == 1 and
         request decoding) first.  Returns next ids (numpy [S]) and optionally
-        logits (numpy [S, vocab])."""
+        logits (numpy [S, vocab]).  temperature 0 takes the argmax; T > 0 draws
+        with bi_sample, keyed by each request's seed, counter = the position of
+        the token drawn."""
         S = len(work)
         n_decode = 0
         while n_decode < S and work[n_decode][0].decoding and work[n_decode][1] == 1:
@@ -179,12 +183,24 @@ class ToyEngine:
                    d_ids.data_ptr(), d_pos.data_ptr(), d_slots.data_ptr(), d_qs.data_ptr(),
                    d_kv.data_ptr(), d_tab.data_ptr(), d_rows.data_ptr())
         stream = torch.cuda.current_stream().cuda_stream
+        sampling = temperature > 0.0
         rc = self.L.bi_toy_step(ctypes.byref(self.c), ctypes.byref(self.w), ctypes.byref(st),
                                    self.ws.data_ptr(), self.ws.numel(), self.next_ids.data_ptr(),
-                                   self.logits.data_ptr() if want_logits else None, stream)
+                                   self.logits.data_ptr() if (want_logits or sampling) else None, stream)
         if rc != 0:
             raise ops.BiError(rc, "bi_toy_step")
-        nxt = self.next_ids[:S].cpu().numpy()
+        if sampling:
+            keys = np.array([[r.seed & (2 ** 64 - 1) for (r, n) in work],
+                             [r.length + n for (r, n) in work]], np.uint64)
+            d_keys = torch.from_numpy(keys.view(np.int64)).to(dev)        # [2, S]: seeds, offsets
+            rc = self.L.bi_sample(self.logits.data_ptr(), self.cfg["vocab"], S, self.cfg["vocab"],
+                                  float(temperature), d_keys[0].data_ptr(), d_keys[1].data_ptr(),
+                                  self.sampled.data_ptr(), stream)
+            if rc != 0:
+                raise ops.BiError(rc, "bi_sample")
+            nxt = self.sampled[:S].cpu().numpy()
+        else:
+            nxt = self.next_ids[:S].cpu().numpy()
         lg = self.logits[:S].cpu().numpy() if want_logits else None
         for s, (r, n) in enumerate(work):
             r.length += n
@@ -201,12 +217,15 @@ def completion_hash(tokens) -> str:
 
 def run_load_experiment(engine: ToyEngine, prompt: np.ndarray, n_runs: int, n_new: int, seed: int,
                         max_active: int = 64, max_step_tokens: int = 1024, other_prompt=(1, 512),
-                        other_new=(1, 256), chunk=(16, 512), progress=None):
-    """Decode `prompt` greedily n_runs times (n_new tokens each) inside a
-    randomly varying continuous batch.  Returns (list of completion hashes,
-    stats).  Each run of the prompt is one request; it shares every step with
-    0..max_active-1 other requests (other runs of the prompt and random
-    requests), arriving and leaving at random, in shuffled order."""
+                        other_new=(1, 256), chunk=(16, 512), progress=None, temperature: float = 0.0,
+                        target_seed: int = 0x5EED):
+    """Decode `prompt` n_runs times (n_new tokens each) inside a randomly
+    varying continuous batch, greedily (temperature 0) or by seeded sampling
+    (every run of the prompt uses target_seed; other requests random seeds).
+    Returns (list of completion hashes, stats).  Each run of the prompt is one
+    request; it shares every step with 0..max_active-1 other requests (other
+    runs of the prompt and random requests), arriving and leaving at random, in
+    shuffled order."""
     g = np.random.default_rng(seed)
     V = engine.cfg["vocab"]
     active: list[Request] = []
@@ -221,15 +240,16 @@ def run_load_experiment(engine: ToyEngine, prompt: np.ndarray, n_runs: int, n_ne
             cap = 1 if g.random() < 0.25 else int(g.integers(2, max_active + 1))
         while len(active) < cap and g.random() < 0.7:
             if targets_started < n_runs and g.random() < 0.5:
-                active.append(Request(rid, prompt, n_new, target=True))
+                active.append(Request(rid, prompt, n_new, target=True, seed=target_seed))
                 targets_started += 1
             else:
                 lp = int(g.integers(other_prompt[0], other_prompt[1] + 1))
                 active.append(Request(rid, g.integers(0, V, lp).astype(np.int32),
-                                      int(g.integers(other_new[0], other_new[1] + 1))))
+                                      int(g.integers(other_new[0], other_new[1] + 1)),
+                                      seed=int(g.integers(0, 2 ** 62))))
             rid += 1
         if not any(r.target for r in active) and targets_started < n_runs and len(active) < max_active:
-            active.append(Request(rid, prompt, n_new, target=True))
+            active.append(Request(rid, prompt, n_new, target=True, seed=target_seed))
             targets_started += 1
             rid += 1
         dec = [r for r in active if r.decoding]
@@ -244,7 +264,7 @@ def run_load_experiment(engine: ToyEngine, prompt: np.ndarray, n_runs: int, n_ne
             n = min(len(r.pending), int(g.integers(chunk[0], chunk[1] + 1)), budget)
             work.append((r, n))
             budget -= n
-        engine.step(work)
+        engine.step(work, temperature=temperature)
         steps += 1
         co_load.append(len(work) - 1)
         for r in list(active):

@@ -96,3 +96,20 @@ def test_nb_toy_experiment_gives_several_completions(nb):
         f"unique completions: {uniq}")
     assert len(hashes) == n_runs
     assert uniq > 1
+
+
+def test_nb_toy_sampled_experiment_gives_several_completions(nb):
+    """The sampled (T = 0.8) experiment on the non-invariant build: the same
+    seeds and schedule as the invariant test give several completions."""
+    from invariant_bi_rmsnorm_amd.toy import ToyEngine, run_load_experiment
+    n_runs = int(os.environ.get("BI_TOY_SAMPLED_RUNS", "300"))
+    w = I.toy_weights(I.TOY)
+    eng = ToyEngine(I.TOY, w, 4096, 1024, 64, 1024)
+    t = time.time()
+    hashes, stats = run_load_experiment(eng, I.toy_prompt(I.TOY, 64), n_runs, 64, seed=5003, progress=log,
+                                        temperature=0.8)
+    uniq = len(set(hashes))
+    log(f"nb sampled toy experiment (T=0.8): {n_runs} runs x 64 tokens in {time.time() - t:.1f}s, {stats}, "
+        f"unique completions: {uniq}")
+    assert len(hashes) == n_runs
+    assert uniq > 1

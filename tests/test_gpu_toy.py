@@ -177,3 +177,20 @@ def test_toy_1000_greedy_runs_collapse_to_one_completion(ops, toy_weights):
     assert len(hashes) == n_runs
     assert stats["co_load_max"] >= 32 and stats["co_load_min"] <= 2
     assert len(uniq) == 1
+
+
+def test_toy_sampled_runs_collapse_to_one_completion(ops, toy_weights):
+    """Seeded sampling at T = 0.8 (every run of the prompt uses one seed; other
+    requests their own): under random co-batched load the runs still give
+    exactly one completion."""
+    from invariant_bi_rmsnorm_amd.toy import run_load_experiment
+    n_runs = int(os.environ.get("BI_TOY_SAMPLED_RUNS", "300"))
+    eng = make_engine(toy_weights)
+    prompt = I.toy_prompt(I.TOY, 64)
+    t = time.time()
+    hashes, stats = run_load_experiment(eng, prompt, n_runs, 64, seed=5003, progress=log, temperature=0.8)
+    uniq = sorted(set(hashes))
+    log(f"sampled toy experiment (T=0.8): {n_runs} runs x 64 tokens in {time.time() - t:.1f}s, {stats}, "
+        f"unique completions: {len(uniq)}")
+    assert len(hashes) == n_runs
+    assert len(uniq) == 1
