@@ -57,6 +57,7 @@ def _load():
     lib.or_argmax.argtypes = [P, I64, I64, I64, P]
     lib.or_log_softmax.argtypes = [P, I64, P, I64, I64, I64]
     lib.or_philox4x32_10.argtypes = [P, P, P, I64]
+    lib.or_top2.argtypes = [P, I64, I64, I64, P, P]
     lib.or_sample.argtypes = [P, I64, I64, I64, ctypes.c_float, P, P, P, P]
     lib.or_num_threads.restype = ctypes.c_int
     lib.or_rope.argtypes = [P, P, P, I64, I32, I32, D]
@@ -265,6 +266,16 @@ def sample(x, temperature: float, seeds, offsets, with_scores: bool = False):
     _load().or_sample(_p(x), V, rows, V, float(np.float32(temperature)), _p(seeds), _p(offsets),
                       _p(ids), _p(sc) if sc is not None else None)
     return (ids, sc) if with_scores else ids
+
+
+def top2(x):
+    """x [rows, V] float32 -> (argmax ids int32 [rows], margins float32 [rows])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, V = x.shape
+    ids = np.empty(rows, np.int32)
+    m = np.empty(rows, np.float32)
+    _load().or_top2(_p(x), V, rows, V, _p(ids), _p(m))
+    return ids, m
 
 
 class _ToyCfg(ctypes.Structure):

@@ -364,6 +364,36 @@ void or_sample(const float* logits, int64_t ld, int64_t rows, int64_t V, float t
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Top-2 logit margin (page arxiv-daily-jp 2609.26621, the precision study:  */
+/* output flips concentrate where the two best candidates are close, and    */
+/* recomputing the head only for such steps was what helped).  Per row: the */
+/* argmax (ties to the lowest index) and margin = top1 - top2, where top2   */
+/* is the largest logit at any other index (so a tie gives 0), computed as  */
+/* one float subtraction; V == 1 gives +inf; a NaN gives id -1, margin NaN. */
+/* ------------------------------------------------------------------------ */
+
+void or_top2(const float* logits, int64_t ld, int64_t rows, int64_t V, int32_t* ids, float* margin)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* x = logits + r * ld;
+        int32_t best = -1;
+        int has_nan = 0;
+        for (int64_t i = 0; i < V; ++i) {
+            if (isnan(x[i])) { has_nan = 1; break; }
+            if (best < 0 || x[i] > x[best]) best = (int32_t)i;
+        }
+        if (has_nan) { ids[r] = -1; margin[r] = NAN; continue; }
+        float second = -INFINITY;
+        int have_second = 0;
+        for (int64_t i = 0; i < V; ++i)
+            if (i != best && (!have_second || x[i] > second)) { second = x[i]; have_second = 1; }
+        ids[r] = best;
+        volatile float top1 = x[best];
+        margin[r] = have_second ? top1 - second : INFINITY;
+    }
+}
+
 int or_num_threads(void)
 {
 #if defined(_OPENMP)

@@ -35,6 +35,7 @@ MUTANTS = {
     "philox_nine_rounds": ("for (int r = 0; r < 10; ++r) {", "for (int r = 0; r < 9; ++r) {"),
     "gumbel_wrong_sign": ("return -log(-log(u));", "return log(-log(u));"),
     "sample_multiplies_by_temperature": ("(double)x[i] / (double)temperature", "(double)x[i] * (double)temperature"),
+    "top2_second_may_be_the_top": ("if (i != best && (!have_second", "if ((!have_second"),
     "toy_no_final_norm": ("or_rmsnorm(h + (T - 1) * H, H, final_norm, xn, H, NULL, 1, H, c->eps);",
                           "memcpy(xn, h + (T - 1) * H, (size_t)H * 2);"),
     "toy_value_from_key_slot": ("memcpy(vv + t * Hkv * D, qkv + t * QKV + (Hq + Hkv) * D",

@@ -469,6 +469,28 @@ def test_sample_small_temperature_is_argmax_and_draws_are_reproducible(orc):
     assert orc.sample(x[3:4], 1.0, seeds[3:4], offs[3:4])[0] == -1
 
 
+# ---------------------------------------------------------------- top-2 margin
+
+def test_top2_margin_cases(orc):
+    x = np.array([[1.0, 5.0, 3.0, 5.0],          # tie at the top: lowest index, margin 0
+                  [0.0, -1.0, 2.5, 2.0],         # 2.5 - 2.0
+                  [7.0, 0.0, 0.0, 0.0],
+                  [-np.inf, -np.inf, 1.0, -np.inf],
+                  [1.0, np.nan, 0.0, 0.0]], np.float32)
+    ids, m = orc.top2(x)
+    assert ids.tolist() == [1, 2, 0, 2, -1]
+    assert m[0] == 0.0 and m[1] == np.float32(0.5) and m[2] == np.float32(7.0) and m[3] == np.inf
+    assert np.isnan(m[4])
+    ids1, m1 = orc.top2(np.array([[3.0]], np.float32))
+    assert ids1[0] == 0 and m1[0] == np.inf                 # no second candidate
+    g = np.random.default_rng(45)
+    x = g.standard_normal((30, 1000)).astype(np.float32)
+    ids, m = orc.top2(x)
+    srt = np.sort(x, axis=1)
+    assert np.array_equal(ids, orc.argmax(x))
+    assert np.array_equal(m, (srt[:, -1] - srt[:, -2]).astype(np.float32))
+
+
 # ---------------------------------------------------------------- sanity
 
 def test_float_addition_order_matters():
