@@ -211,6 +211,18 @@ int bi_sample(const float* logits, int64_t ld, int64_t rows, int64_t V, float te
               const uint64_t* seeds, const uint64_t* offsets, int32_t* ids, void* stream);
 
 /*
+ * Top-2 logit margin monitor (page arxiv-daily-jp 2609.26621: output flips
+ * concentrate where the two best candidates are close, and recomputing the
+ * head only for such steps is what helped).  ids[r] = argmax of row r (ties
+ * to the lowest index, as bi_argmax); margin[r] = top1 - top2 in fp32, top2
+ * the largest logit at any other index (a tie gives 0); V == 1 gives +inf; a
+ * NaN gives -1 and NaN.  Both are order-free (maxima and a total order).
+ * logits [rows][ld] fp32, ids [rows] int32, margin [rows] fp32, device.
+ */
+int bi_top2(const float* logits, int64_t ld, int64_t rows, int64_t V, int32_t* ids, float* margin,
+            void* stream);
+
+/*
  * Greedy token choice (temperature 0 = argmax at every step; page
  * "la température zéro n'est pas déterministe", section "Le mensonge de la
  * température zéro").  ids[r] = index of the largest logit of row r, ties to

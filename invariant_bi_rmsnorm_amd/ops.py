@@ -21,6 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("BI_LIB") or os.path.join(_HERE, "libbi.so")
 # non-invariant baseline library (same ABI); see use_library()
 NB_LIB_PATH = os.path.join(_HERE, "libbi_nb.so")
+DEFAULT_LIB_PATH = LIB_PATH
 
 BI_OK = 0
 BI_ERR_INVALID_ARGUMENT = 1
@@ -51,6 +52,7 @@ SIGNATURES = {
     "bi_argmax": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
     "bi_log_softmax": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P]),
     "bi_sample": (ctypes.c_int, [_P, _I64, _I64, _I64, _F, _P, _P, _P, _P]),
+    "bi_top2": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "bi_probe_mfma_bf16": (ctypes.c_int, [_P, _P, _P, _P]),
     "bi_probe_copy": (ctypes.c_int, [_P, _P, _I64, _P]),
     # include/bi_toy.h
@@ -345,6 +347,17 @@ def bi_sample(logits: torch.Tensor, temperature: float, seeds: torch.Tensor, off
     _check(lib().bi_sample(_ptr(logits), _ld(logits), rows, V, float(temperature), _ptr(seeds),
                            _ptr(offsets), _ptr(ids), _stream(stream)), "bi_sample")
     return ids
+
+
+def bi_top2(logits: torch.Tensor, stream=None):
+    """(argmax ids int32 [rows], top1 - top2 margins fp32 [rows]) of logits [rows, V] fp32."""
+    _need(logits, torch.float32, "logits")
+    rows, V = logits.shape
+    ids = torch.empty((rows,), dtype=torch.int32, device=logits.device)
+    margin = torch.empty((rows,), dtype=torch.float32, device=logits.device)
+    _check(lib().bi_top2(_ptr(logits), _ld(logits), rows, V, _ptr(ids), _ptr(margin), _stream(stream)),
+           "bi_top2")
+    return ids, margin
 
 
 def bi_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):

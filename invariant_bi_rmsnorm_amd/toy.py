@@ -218,11 +218,12 @@ def completion_hash(tokens) -> str:
 def run_load_experiment(engine: ToyEngine, prompt: np.ndarray, n_runs: int, n_new: int, seed: int,
                         max_active: int = 64, max_step_tokens: int = 1024, other_prompt=(1, 512),
                         other_new=(1, 256), chunk=(16, 512), progress=None, temperature: float = 0.0,
-                        target_seed: int = 0x5EED):
+                        target_seed: int = 0x5EED, tokens_out: list | None = None):
     """Decode `prompt` n_runs times (n_new tokens each) inside a randomly
     varying continuous batch, greedily (temperature 0) or by seeded sampling
     (every run of the prompt uses target_seed; other requests random seeds).
-    Returns (list of completion hashes, stats).  Each run of the prompt is one
+    Returns (list of completion hashes, stats); with tokens_out, the token lists
+    of the runs are appended there too.  Each run of the prompt is one
     request; it shares every step with 0..max_active-1 other requests (other
     runs of the prompt and random requests), arriving and leaving at random, in
     shuffled order."""
@@ -271,6 +272,8 @@ def run_load_experiment(engine: ToyEngine, prompt: np.ndarray, n_runs: int, n_ne
             if r.done:
                 if r.target:
                     results.append(completion_hash(r.generated[:n_new]))
+                    if tokens_out is not None:
+                        tokens_out.append(list(r.generated[:n_new]))
                 engine.release(r)
                 active.remove(r)
         if progress and steps % 500 == 0:

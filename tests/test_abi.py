@@ -210,3 +210,11 @@ def test_sample_validation(L):
     assert f(A16, 100, 2, 100, float("nan"), A16, A16, A16, None) == 1
     assert f(A16, 100, 2, 100, 1.0, None, A16, A16, None) == 1         # null seeds
     assert f(A16, 100, 2, 100, 1.0, A16 + 4, A16, A16, None) == 1      # misaligned seeds
+
+
+def test_top2_validation(L):
+    f = L.bi_top2
+    assert f(A16, 100, 0, 100, A16, A16, None) == 0
+    assert f(A16, 99, 2, 100, A16, A16, None) == 1
+    assert f(A16, 100, 2, 100, A16, None, None) == 1
+    assert f(A16 + 2, 100, 2, 100, A16, A16, None) == 1

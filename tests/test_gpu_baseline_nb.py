@@ -113,3 +113,41 @@ def test_nb_toy_sampled_experiment_gives_several_completions(nb):
         f"unique completions: {uniq}")
     assert len(hashes) == n_runs
     assert uniq > 1
+
+
+def test_nb_flips_happen_where_the_top2_margin_is_small(nb):
+    """Where the non-invariant build's completions first leave the invariant
+    one, the invariant trajectory's top-1/top-2 logit margin (bi_top2) is
+    small: the flips the pages count are near-ties of the two best tokens."""
+    from invariant_bi_rmsnorm_amd import ops as o
+    from invariant_bi_rmsnorm_amd.toy import Request, ToyEngine, run_load_experiment
+    w = I.toy_weights(I.TOY)
+    prompt = I.toy_prompt(I.TOY, 64)
+    n_new = 256
+    # invariant reference, alone, with the margin of every step
+    prev = o.use_library(o.DEFAULT_LIB_PATH)
+    try:
+        ref_eng = ToyEngine(I.TOY, w, 4096, 1024, 64, 1024)
+        r = Request(0, prompt, n_new)
+        margins = []
+        work = [(r, len(prompt))]
+        while not r.done:
+            ref_eng.step(work, want_logits=True)
+            _, m = o.bi_top2(ref_eng.logits[:1])
+            margins.append(float(m.item()))
+            work = [(r, 1)]
+        ref = list(r.generated)
+    finally:
+        o.use_library(prev)
+    margins = np.array(margins)
+    # the non-invariant build under load
+    eng = ToyEngine(I.TOY, w, 4096, 1024, 64, 1024)
+    toks = []
+    run_load_experiment(eng, prompt, 300, n_new, seed=5002, tokens_out=toks)
+    firsts = sorted({next(i for i, (a, b) in enumerate(zip(t, ref)) if a != b) for t in toks if t != ref})
+    flip_m = margins[firsts] if firsts else np.array([])
+    log(f"nb flips: first divergence at steps {firsts[:20]}; invariant margins there "
+        f"{np.round(flip_m, 4).tolist()[:20]}; median margin over all {len(margins)} steps "
+        f"{np.median(margins):.3f}")
+    assert len(firsts) > 0
+    assert np.max(flip_m) < np.median(margins)

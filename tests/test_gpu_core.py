@@ -358,3 +358,21 @@ def test_sample_batch_invariance(ops):
         x[p], seeds[p], offs[p] = row, seed, off
         got = ops.bi_sample(torch.from_numpy(x).cuda(), 0.8, _u64(seeds), _u64(offs)).cpu().numpy()
         assert got[p] == alone, f"B={B} p={p}"
+
+
+# ------------------------------------------------------------------ top-2 margin
+
+@pytest.mark.parametrize("V", [1, 2, 255, 1000, 32000, 70001])
+def test_top2_matches_oracle(ops, orc, V):
+    g = np.random.default_rng(900 + V)
+    x = g.standard_normal((50, V)).astype(np.float32)
+    if V > 3:
+        for r in range(0, 50, 5):                     # planted top ties -> margin 0
+            i, j = sorted(g.choice(V, 2, replace=False))
+            x[r, i] = x[r, j] = x[r].max() + 1.0
+        x[7, ::2] = -np.inf
+        x[9, V // 3] = np.nan
+    ids, m = ops.bi_top2(torch.from_numpy(x).cuda())
+    rid, rm = orc.top2(x)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.array_equal(m.cpu().numpy().view(np.uint32), rm.view(np.uint32))
