@@ -20,14 +20,16 @@
 // The one configuration (chosen by measuring the whole M = 1..2048 sweep of
 // Llama-8B projections on MI355X; small M is weight-streaming, large M is
 // MFMA/L2 bound, and one tile has to serve both):
-//   * workgroup tile 64 (m) x 64 (n) x 256 (k), 512 threads = 8 wavefronts in
-//     a 4 (m) x 2 (n) arrangement, each wavefront 16x32 outputs as 1x2 MFMA
-//     tiles (eight wavefronts keep more loads in flight per CU than four,
-//     which is what the weight-streaming small-M shapes are bound by);
+//   * workgroup tile 64 (m) x 32 (n) x 128 (k), 512 threads = 8 wavefronts in
+//     a 4 (m) x 2 (n) arrangement, each wavefront one 16x16 MFMA tile; small
+//     N-tiles give the weight-streaming small-M shapes more workgroups (a
+//     CU streams from HBM at a bounded rate, so the number of CUs at work is
+//     what sets their speed: N = 4096 gives 128 workgroups);
 //   * operands go global -> LDS with global_load_lds_dwordx4 (no register
-//     staging), two stages, so one 64 KB stage is in flight while the other is
-//     consumed; a row's 256-wide k slice is 512 contiguous bytes in HBM;
-//   * LDS rows are 512 B with the 16-byte chunks XOR-swizzled by (row & 7),
+//     staging), three 24 KB stages (two in flight while one is consumed),
+//     72 KB in all, so two workgroups share a CU at large M; a row's 128-wide
+//     k slice is 256 contiguous bytes in HBM;
+//   * LDS rows are 256 B with the 16-byte chunks XOR-swizzled by (row & 7),
 //     so the 16 rows an MFMA operand read touches fall in different banks;
 //   * tiles are dealt to the 8 XCDs in contiguous ranges of a grouped order
 //     (bands of 4 m-tiles, n-major inside a band), so the wavefronts running

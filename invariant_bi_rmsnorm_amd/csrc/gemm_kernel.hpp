@@ -10,11 +10,11 @@
 namespace {
 
 constexpr int kBM = 64;
-constexpr int kBN = 64;
-constexpr int kBK = 256;
+constexpr int kBN = 32;
+constexpr int kBK = 128;
 constexpr int kWM = 4;
 constexpr int kWN = 2;
-constexpr int kStages = 2;
+constexpr int kStages = 3;
 constexpr int kGroup = 4;                         // m-tiles per band of the tile order
 constexpr int kWaves = kWM * kWN;
 constexpr int kThreads = 64 * kWaves;
