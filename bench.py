@@ -486,6 +486,58 @@ def main():
                                   "cores": oracle.num_threads(), "kind": "oracle",
                                   "sample": f"oracle matmul (fp64) of {rows} rows of the M=2048 "
                                             f"[M,4096]x[4096,14336] GEMM, {dt:.1f} s"}
+
+        # the oracle beside the other rows, on bounded samples of the same work
+        # (GPU times from this run: the instrumented sweep and the supplementary points)
+        beside = {}
+        try:
+
+            def timed(fn):
+                t0 = time.perf_counter()
+                fn()
+                return time.perf_counter() - t0
+
+            rms_2048 = [a.elapsed_time(b) * 1e3 for (a, b, M) in rec["rms"] if M == 2048]
+            dt = timed(lambda: oracle.rmsnorm(I.llama_x(2048), I.llama_norm_weight(), I.LLAMA_EPS))
+            beside["rmsnorm_2048x4096"] = {"cpu_s": round(dt, 3), "gpu_us": round(float(np.median(rms_2048)), 2)}
+            sup = result.get("supplementary", {})
+            if "log_softmax_256x32000" in sup:
+                xl = (np.random.default_rng(7).standard_normal((256, 32000)) * 3).astype(np.float32)
+                beside["log_softmax_256x32000"] = {"cpu_s": round(timed(lambda: oracle.log_softmax(xl)), 3),
+                                                   "gpu_us": sup["log_softmax_256x32000"]["us"]}
+            if "decode_S_sweep" in sup:
+                Sd = 16
+                qh = I.queries(I.TAG_DECODE, 0, S_DEC)
+
+                def decode_oracle():
+                    for s_ in range(Sd):
+                        L_ = int(lens[s_])
+                        nb_ = -(-L_ // 16)
+                        blk = torch.from_numpy(table[s_, :nb_].astype(np.int64)).to(dev)
+                        kh = kc[blk].permute(0, 2, 1, 3).reshape(nb_ * 16, I.ATT_HKV, I.ATT_D)[:L_]
+                        vh = vc[blk].permute(0, 3, 1, 2).reshape(nb_ * 16, I.ATT_HKV, I.ATT_D)[:L_]
+                        oracle.attention(qh[s_][None], [L_ - 1], kh.contiguous().view(torch.int16).cpu().numpy().view(np.uint16),
+                                         vh.contiguous().view(torch.int16).cpu().numpy().view(np.uint16), scale)
+                gpu_row = [r for r in sup["decode_S_sweep"]["rows"] if r["S"] == Sd][0]
+                beside["decode_S16"] = {"cpu_s": round(timed(decode_oracle), 3), "gpu_us": gpu_row["us"],
+                                        "kv_tokens": gpu_row["kv_tokens"],
+                                        "note": "cpu_s includes copying those sequences' K/V to the host"}
+            if "prefill_P_sweep" in sup:
+                P_ = 512
+                kh = pk[torch.from_numpy(ptable[0, :P_ // 16].astype(np.int64)).to(dev)]
+                vh = pv[torch.from_numpy(ptable[0, :P_ // 16].astype(np.int64)).to(dev)]
+                kh = kh.permute(0, 2, 1, 3).reshape(P_, I.ATT_HKV, I.ATT_D).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                vh = vh.permute(0, 3, 1, 2).reshape(P_, I.ATT_HKV, I.ATT_D).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                qp = pq[:P_].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                gpu_row = [r for r in sup["prefill_P_sweep"] if r["P"] == P_ and "chunks" not in r][0]
+                beside["prefill_P512"] = {"cpu_s": round(timed(lambda: oracle.attention(qp, np.arange(P_), kh, vh,
+                                                                                         scale)), 3),
+                                          "gpu_us": gpu_row["us"]}
+            for v_ in beside.values():
+                v_["cpu_over_gpu"] = round(v_["cpu_s"] / (v_["gpu_us"] * 1e-6), 1)
+        except Exception as e:  # context only: never lose the result line for it
+            beside["error"] = f"{type(e).__name__}: {e}"[:300]
+        result["cpu_oracle_beside"] = beside
     print(json.dumps(result), flush=True)
 
 
