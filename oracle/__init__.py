@@ -56,6 +56,7 @@ def _load():
     lib.or_attention.argtypes = [P, I64, P, P, P, I64, I32, I32, I32, D, P, P, P]
     lib.or_argmax.argtypes = [P, I64, I64, I64, P]
     lib.or_log_softmax.argtypes = [P, I64, P, I64, I64, I64]
+    lib.or_mean.argtypes = [P, I64, P, I64, I64]
     lib.or_philox4x32_10.argtypes = [P, P, P, I64]
     lib.or_top2.argtypes = [P, I64, I64, I64, P, P]
     lib.or_sample.argtypes = [P, I64, I64, I64, ctypes.c_float, P, P, P, P]
@@ -233,6 +234,15 @@ def add(a, b):
     a = _u16(a); b = _u16(b)
     out = np.empty_like(a)
     _load().or_add(_p(a), _p(b), _p(out), a.size)
+    return out
+
+
+def mean(x):
+    """x [rows, H] bf16 bits -> row means, float64 [rows]."""
+    x = _u16(x)
+    rows, H = x.shape
+    out = np.empty(rows, np.float64)
+    _load().or_mean(_p(x), H, _p(out), rows, H)
     return out
 
 

@@ -266,6 +266,23 @@ void or_argmax(const float* logits, int64_t ld, int64_t rows, int64_t V, int32_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* Mean over the last dimension (post "論文／ブログ「Defeating Nondeterminism   */
+/* in LLM Inference」の技術的なポイント", section 他の演算子（RMSNorm, MatMul,    */
+/* mean/reduction etc.）: torch.mean is one of the reductions whose order the */
+/* invariant library fixes).  out_r = (1/H) * sum_j x_rj, bf16 in, double.   */
+/* ------------------------------------------------------------------------ */
+
+void or_mean(const uint16_t* x, int64_t ldx, double* out, int64_t rows, int64_t H)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double s = 0.0;
+        for (int64_t j = 0; j < H; ++j) s += bf16_bits_to_double(x[r * ldx + j]);
+        out[r] = s / (double)H;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* log_softmax over the last dimension.  The page post "論文／ブログ          */
 /* 「Defeating Nondeterminism in LLM Inference」の技術的なポイント", section     */
 /* 他の演算子（RMSNorm, MatMul, mean/reduction etc.）, lists log_softmax among */

@@ -349,6 +349,25 @@ def test_argmax_ties_lowest_index_and_nan(orc):
     assert orc.argmax(x[7:8])[0] == -1
 
 
+# ---------------------------------------------------------------- mean
+
+def test_mean_closed_forms_and_brute_force(orc):
+    H = 4096
+    x = np.zeros((4, H), np.uint16)
+    x[0] = bits_of([1.5])[0]                                   # constant row
+    x[1, 17] = bits_of([1.0])[0]                               # one-hot: 1/H
+    x[2, :H // 2] = bits_of([2.0])[0]
+    x[2, H // 2:] = bits_of([-2.0])[0]                         # cancels to 0
+    x[3] = bits_of(np.arange(H) % 7 - 3.0)                     # small integers
+    m = orc.mean(x)
+    assert m[0] == 1.5 and m[1] == 1.0 / H and m[2] == 0.0
+    assert m[3] == float(Fraction(int(np.sum(np.arange(H) % 7 - 3)), H))
+    g = np.random.default_rng(46)
+    y = I.normal_bf16(g, (5, 33))
+    ref = [sum((F(b) for b in row), Fraction(0)) / 33 for row in y]
+    assert np.allclose(orc.mean(y), [float(r) for r in ref], rtol=1e-15, atol=0)
+
+
 # ---------------------------------------------------------------- log_softmax
 
 def test_log_softmax_uniform_row_is_minus_log_V(orc):
