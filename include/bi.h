@@ -173,6 +173,18 @@ int bi_attention_prefill(const void* q, int64_t ldq, const int32_t* q_start,
                          void* stream);
 
 /*
+ * Mean over the last dimension, batch-invariant (post "論文／ブログ「Defeating
+ * Nondeterminism in LLM Inference」の技術的なポイント", section 他の演算子
+ * （RMSNorm, MatMul, mean/reduction etc.）: torch.mean is one of the reductions
+ * whose order must not follow the batch).  out[r] = (1/H) sum_j x[r][j] with
+ * the RMSNorm kernel's reduction order (fixed by H alone).
+ *
+ * x [rows][ldx] bf16 (16-byte aligned, ldx % 8 == 0), out [rows] fp32, device
+ * pointers.  H % 8 == 0 and H <= 16384, else BI_ERR_UNSUPPORTED.
+ */
+int bi_mean(const void* x, int64_t ldx, float* out, int64_t rows, int64_t H, void* stream);
+
+/*
  * log_softmax over the last dimension, batch-invariant (post "論文／ブログ
  * 「Defeating Nondeterminism in LLM Inference」の技術的なポイント", section
  * 他の演算子（RMSNorm, MatMul, mean/reduction etc.）: log_softmax is one of the

@@ -51,6 +51,7 @@ SIGNATURES = {
                                             _I32, _I64, _I32, _I32, _I32, _I32, _F, _P]),
     "bi_argmax": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
     "bi_log_softmax": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P]),
+    "bi_mean": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P]),
     "bi_sample": (ctypes.c_int, [_P, _I64, _I64, _I64, _F, _P, _P, _P, _P]),
     "bi_top2": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "bi_probe_mfma_bf16": (ctypes.c_int, [_P, _P, _P, _P]),
@@ -317,6 +318,17 @@ def bi_argmax(logits: torch.Tensor, ids: torch.Tensor = None, stream=None) -> to
     _check(lib().bi_argmax(_ptr(logits), _ld(logits), rows, V, _ptr(ids), _stream(stream)),
            "bi_argmax")
     return ids
+
+
+def bi_mean(x: torch.Tensor, out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """Row means of x [rows, H] (bf16) as fp32 [rows]."""
+    _need(x, torch.bfloat16, "x")
+    rows, H = x.shape
+    if out is None:
+        out = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _need_dense(out, torch.float32, (rows,), "out")
+    _check(lib().bi_mean(_ptr(x), _ld(x), _ptr(out), rows, H, _stream(stream)), "bi_mean")
+    return out
 
 
 def bi_log_softmax(x: torch.Tensor, out: torch.Tensor = None, stream=None) -> torch.Tensor:

@@ -218,3 +218,13 @@ def test_top2_validation(L):
     assert f(A16, 99, 2, 100, A16, A16, None) == 1
     assert f(A16, 100, 2, 100, A16, None, None) == 1
     assert f(A16 + 2, 100, 2, 100, A16, A16, None) == 1
+
+
+def test_mean_validation(L):
+    f = L.bi_mean
+    assert f(A16, 4096, A16, 0, 4096, None) == 0
+    assert f(A16, 4000, A16, 2, 4096, None) == 1       # ldx < H
+    assert f(MIS, 4096, A16, 2, 4096, None) == 1
+    assert f(A16, 4100, A16, 2, 4100, None) == 1       # ldx % 8
+    assert f(A16, 4096, A16, 2, 4092, None) == 2       # H % 8
+    assert f(A16, 32768, A16, 2, 32768, None) == 2     # H > 16384

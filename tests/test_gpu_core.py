@@ -376,3 +376,23 @@ def test_top2_matches_oracle(ops, orc, V):
     rid, rm = orc.top2(x)
     assert np.array_equal(ids.cpu().numpy(), rid)
     assert np.array_equal(m.cpu().numpy().view(np.uint32), rm.view(np.uint32))
+
+
+# ------------------------------------------------------------------ mean
+
+@pytest.mark.parametrize("H", [8, 256, 2056, 4096, 16384])
+def test_mean_parity_and_batch_invariance(ops, orc, H):
+    g = np.random.default_rng(300 + H)
+    x = I.normal_bf16(g, (37, H), 0.5, 2.0)
+    got = ops.bi_mean(dev_bf16(x)).cpu().numpy()
+    ref = orc.mean(x)
+    # fp32: at most 2^-24 per add over 64 sequential adds and 8 tree levels,
+    # relative to the sum of magnitudes; bar 1e-5 of mean|x| per row
+    scale = np.mean(np.abs(I.bf16_to_f32(x).astype(np.float64)), axis=1)
+    assert np.all(np.abs(got - ref) <= 1e-5 * scale)
+    row, ref_bits = x[5], got[5:6].view(np.uint32)[0]
+    for B in (1, 2, 9, 64):
+        xb = I.normal_bf16(g, (B, H))
+        p = int(g.integers(0, B))
+        xb[p] = row
+        assert ops.bi_mean(dev_bf16(xb)).cpu().numpy()[p:p + 1].view(np.uint32)[0] == ref_bits, (B, p)
