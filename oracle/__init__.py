@@ -53,6 +53,7 @@ def _load():
     lib.or_rmsnorm_f64.argtypes = [P, I64, P, P, I64, P, I64, I64, D]
     lib.or_matmul.argtypes = [P, I64, P, I64, P, I64, ctypes.c_int, I64, I64, I64]
     lib.or_matmul_f64.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64]
+    lib.or_addmm_f64.argtypes = [P, I64, P, I64, P, P, I64, I64, I64, I64]
     lib.or_attention.argtypes = [P, I64, P, P, P, I64, I32, I32, I32, D, P, P, P]
     lib.or_argmax.argtypes = [P, I64, I64, I64, P]
     lib.or_log_softmax.argtypes = [P, I64, P, I64, I64, I64]
@@ -160,6 +161,18 @@ def matmul_f64(a, wt):
         raise ValueError("inner dimensions differ")
     c = np.empty((M, N), dtype=np.float64)
     _load().or_matmul_f64(_p(a), K, _p(wt), K, _p(c), N, M, N, K)
+    return c
+
+
+def addmm_f64(a, wt, bias):
+    """bias [N] + a [M,K] @ wt[N,K]^T, all bf16 bits, in float64."""
+    a = _u16(a); wt = _u16(wt); bias = _u16(bias)
+    M, K = a.shape
+    N, K2 = wt.shape
+    if K != K2 or bias.shape != (N,):
+        raise ValueError("shapes")
+    c = np.empty((M, N), dtype=np.float64)
+    _load().or_addmm_f64(_p(a), K, _p(wt), K, _p(bias), _p(c), N, M, N, K)
     return c
 
 

@@ -158,6 +158,19 @@ void or_matmul_f64(const uint16_t* a, int64_t lda, const uint16_t* wt, int64_t l
     }
 }
 
+/* Matmul plus a bias row (torch.addmm with alpha = beta = 1, which the post */
+/* "論文／ブログ「Defeating Nondeterminism in LLM Inference」の技術的なポイント",   */
+/* section 他の演算子（RMSNorm, MatMul, mean/reduction etc.）, lists among the  */
+/* ops replaced by invariant kernels): c[m][n] = bias[n] + sum_k a[m][k] w[n][k], */
+/* exact in double (the bf16 products and the bias are exact there).          */
+void or_addmm_f64(const uint16_t* a, int64_t lda, const uint16_t* wt, int64_t ldw,
+                  const uint16_t* bias, double* c, int64_t ldc, int64_t M, int64_t N, int64_t K)
+{
+    or_matmul_f64(a, lda, wt, ldw, c, ldc, M, N, K);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) c[m * ldc + n] += bf16_bits_to_double(bias[n]);
+}
+
 /* c_f32 != 0: C is float (one rounding double -> binary32);
  * c_f32 == 0: C is bf16 (one rounding double -> bf16). */
 void or_matmul(const uint16_t* a, int64_t lda, const uint16_t* wt, int64_t ldw,

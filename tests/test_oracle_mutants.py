@@ -29,6 +29,8 @@ MUTANTS = {
     "silu_wrong_sign": ("gv / (1.0 + exp(-gv))", "gv / (1.0 + exp(gv))"),
     "add_subtracts": ("bf16_bits_to_double(a[i]) + bf16_bits_to_double(b[i])",
                       "bf16_bits_to_double(a[i]) - bf16_bits_to_double(b[i])"),
+    "addmm_subtracts_bias": ("c[m * ldc + n] += bf16_bits_to_double(bias[n]);", "c[m * ldc + n] -= bf16_bits_to_double(bias[n]);"),
+    "addmm_bias_by_row": ("c[m * ldc + n] += bf16_bits_to_double(bias[n]);", "c[m * ldc + n] += bf16_bits_to_double(bias[m % N]);"),
     "mean_over_H_plus_1": ("out[r] = s / (double)H;", "out[r] = s / (double)(H + 1);"),
     "log_softmax_drops_max": ("const double lse = m + log(s);", "const double lse = log(s);"),
     "log_softmax_drops_first_term": ("for (int64_t i = 0; i < V; ++i) s += exp", "for (int64_t i = 1; i < V; ++i) s += exp"),

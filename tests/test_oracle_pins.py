@@ -349,6 +349,19 @@ def test_argmax_ties_lowest_index_and_nan(orc):
     assert orc.argmax(x[7:8])[0] == -1
 
 
+# ---------------------------------------------------------------- addmm
+
+def test_addmm_bias_row_added_once(orc):
+    g = np.random.default_rng(47)
+    a = bits_of(g.integers(-8, 9, (5, 64)).astype(np.float64))
+    w = bits_of(g.integers(-8, 9, (7, 64)).astype(np.float64))
+    b = bits_of(g.integers(-100, 101, 7).astype(np.float64) / 4)
+    exact = (I.bf16_to_f32(a).astype(np.int64) @ I.bf16_to_f32(w).astype(np.int64).T).astype(np.float64) \
+        + I.bf16_to_f32(b).astype(np.float64)[None]
+    assert np.array_equal(orc.addmm_f64(a, w, b), exact)
+    assert np.array_equal(orc.addmm_f64(np.zeros_like(a), w, b)[3], I.bf16_to_f32(b).astype(np.float64))
+
+
 # ---------------------------------------------------------------- mean
 
 def test_mean_closed_forms_and_brute_force(orc):
