@@ -100,6 +100,18 @@ int bi_matmul(const void* a, int64_t lda, const void* wt, int64_t ldw,
               void* stream);
 
 /*
+ * addmm (torch.addmm with alpha = beta = 1, one of the ops the post
+ * "論文／ブログ「Defeating Nondeterminism in LLM Inference」の技術的なポイント",
+ * section 他の演算子（RMSNorm, MatMul, mean/reduction etc.）, lists as replaced
+ * by invariant kernels): c[m][n] = bias[n] + sum_k a[m][k] * wt[n][k].  The
+ * same kernel and K chain as bi_matmul; the bf16 bias is added to the fp32
+ * chain result once, then the output is rounded.  bias [N] bf16, device,
+ * 8-byte aligned; every other argument as bi_matmul.
+ */
+int bi_addmm(const void* a, int64_t lda, const void* wt, int64_t ldw, const void* bias, void* c,
+             int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * Append fresh keys/values to the paged cache, so that attention reads cached
  * and fresh tokens through one layout (table row アテンション (Attention) of the
  * same section: merge cache and current data into one consistent layout before

@@ -1,4 +1,4 @@
-// nb_gemm.hip -- NON-invariant baseline of bi_matmul, built only into
+// nb_gemm.hip -- NON-invariant baseline of bi_matmul and bi_addmm, built only into
 // libbi_nb.so for measurement and for checking that the invariance tests can
 // see a batch-dependent strategy.
 //
@@ -18,7 +18,19 @@ extern "C" int bi_matmul(const void* a, int64_t lda, const void* wt, int64_t ldw
     BI_TRY_BEGIN
     const int v = gemm_validate(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K);
     if (v != BI_OK) return v < 0 ? BI_OK : v;
-    if (M <= 128) return gemm_launch<1>(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K, stream);
-    return gemm_launch<0>(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K, stream);
+    if (M <= 128) return gemm_launch<1>(a, lda, wt, ldw, nullptr, c, ldc, c_dtype, M, N, K, stream);
+    return gemm_launch<0>(a, lda, wt, ldw, nullptr, c, ldc, c_dtype, M, N, K, stream);
+    BI_TRY_END
+}
+
+extern "C" int bi_addmm(const void* a, int64_t lda, const void* wt, int64_t ldw, const void* bias, void* c,
+                        int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, void* stream)
+{
+    BI_TRY_BEGIN
+    const int v = gemm_validate(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K);
+    if (v != BI_OK) return v < 0 ? BI_OK : v;
+    if (!bias || !bi_aligned(bias, 8)) return BI_ERR_INVALID_ARGUMENT;
+    if (M <= 128) return gemm_launch<1>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    return gemm_launch<0>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     BI_TRY_END
 }

@@ -45,6 +45,19 @@ extern "C" int bi_matmul(const void* a, int64_t lda, const void* wt, int64_t ldw
     BI_TRY_BEGIN
     const int v = gemm_validate(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K);
     if (v != BI_OK) return v < 0 ? BI_OK : v;
-    return gemm_launch<0>(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K, stream);
+    return gemm_launch<0>(a, lda, wt, ldw, nullptr, c, ldc, c_dtype, M, N, K, stream);
+    BI_TRY_END
+}
+
+// addmm: the same kernel and K chain, the bias row added to the fp32 result
+// once, before the output rounding.
+extern "C" int bi_addmm(const void* a, int64_t lda, const void* wt, int64_t ldw, const void* bias, void* c,
+                        int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, void* stream)
+{
+    BI_TRY_BEGIN
+    const int v = gemm_validate(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K);
+    if (v != BI_OK) return v < 0 ? BI_OK : v;
+    if (!bias || !bi_aligned(bias, 8)) return BI_ERR_INVALID_ARGUMENT;
+    return gemm_launch<0>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     BI_TRY_END
 }

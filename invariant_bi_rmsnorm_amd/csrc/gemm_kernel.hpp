@@ -65,7 +65,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7
 template <int kOrder>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* __restrict__ a, int64_t lda, const uint16_t* __restrict__ wt, int64_t ldw,
-    void* __restrict__ c, int64_t ldc, int c_f32, int M, int N, int K)
+    const uint16_t* __restrict__ bias, void* __restrict__ c, int64_t ldc, int c_f32, int M, int N, int K)
 {
     __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * (kStageA + kStageW)];
 
@@ -200,6 +200,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
             if (m < M && n < N) {
                 f32x4 v = acc[i][j];
                 if (kOrder == 1) v = v + acc2[i][j];
+                if (bias) {                               // addmm: the bias row, after the whole chain
+                    const u32x2 bb = *reinterpret_cast<const u32x2*>(bias + n);
+                    v[0] = v[0] + bf16_to_f32(bb[0] & 0xffffu);
+                    v[1] = v[1] + bf16_to_f32(bb[0] >> 16);
+                    v[2] = v[2] + bf16_to_f32(bb[1] & 0xffffu);
+                    v[3] = v[3] + bf16_to_f32(bb[1] >> 16);
+                }
                 if (c_f32) {
                     *reinterpret_cast<f32x4*>((float*)c + (int64_t)m * ldc + n) = v;
                 } else {
@@ -236,13 +243,14 @@ static inline int gemm_validate(const void* a, int64_t lda, const void* wt, int6
 }
 
 template <int kOrder>
-static inline int gemm_launch(const void* a, int64_t lda, const void* wt, int64_t ldw, void* c,
-                              int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, void* stream)
+static inline int gemm_launch(const void* a, int64_t lda, const void* wt, int64_t ldw, const void* bias,
+                              void* c, int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K,
+                              void* stream)
 {
     const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
     const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
     hipLaunchKernelGGL(gemm_kernel<kOrder>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
-                       (const uint16_t*)a, lda, (const uint16_t*)wt, ldw, c, ldc,
+                       (const uint16_t*)a, lda, (const uint16_t*)wt, ldw, (const uint16_t*)bias, c, ldc,
                        c_dtype == BI_F32 ? 1 : 0, (int)M, (int)N, (int)K);
     return bi_launch_status();
 }

@@ -43,6 +43,7 @@ SIGNATURES = {
     "bi_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bi_rmsnorm": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _I64, _I64, _F, _P]),
     "bi_matmul": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, ctypes.c_int, _I64, _I64, _I64, _P]),
+    "bi_addmm": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _I64, ctypes.c_int, _I64, _I64, _I64, _P]),
     "bi_kv_append": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _P, _I64, _I32, _I32, _P]),
     "bi_attention_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "bi_attention_decode": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _I32, _P, _P, _I64,
@@ -207,6 +208,28 @@ def bi_matmul(a: torch.Tensor, wt: torch.Tensor, out_dtype=torch.bfloat16, c: to
         raise ValueError(f"c must have shape {(M, N)}")
     _check(lib().bi_matmul(_ptr(a), _ld(a), _ptr(wt), _ld(wt), _ptr(c), _ld(c), code, M, N, K,
                            _stream(stream)), "bi_matmul")
+    return c
+
+
+def bi_addmm(a: torch.Tensor, wt: torch.Tensor, bias: torch.Tensor, out_dtype=torch.bfloat16,
+             c: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """c = bias + a @ wt.T with wt stored [N, K], bias [N] (bf16)."""
+    _need(a, torch.bfloat16, "a"); _need(wt, torch.bfloat16, "wt")
+    M, K = a.shape
+    N, K2 = wt.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    _need_dense(bias, torch.bfloat16, (N,), "bias")
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    code = BI_BF16 if c.dtype == torch.bfloat16 else BI_F32 if c.dtype == torch.float32 else None
+    if code is None:
+        raise ValueError("c must be bfloat16 or float32")
+    _need(c, c.dtype, "c")
+    if tuple(c.shape) != (M, N):
+        raise ValueError(f"c must have shape {(M, N)}")
+    _check(lib().bi_addmm(_ptr(a), _ld(a), _ptr(wt), _ld(wt), _ptr(bias), _ptr(c), _ld(c), code, M, N, K,
+                          _stream(stream)), "bi_addmm")
     return c
 
 

@@ -228,3 +228,11 @@ def test_mean_validation(L):
     assert f(A16, 4100, A16, 2, 4100, None) == 1       # ldx % 8
     assert f(A16, 4096, A16, 2, 4092, None) == 2       # H % 8
     assert f(A16, 32768, A16, 2, 32768, None) == 2     # H > 16384
+
+
+def test_addmm_validation(L):
+    f = L.bi_addmm
+    assert f(A16, 4096, A16, 4096, A16, A16, 4096, 0, 0, 8, 4096, None) == 0     # M == 0
+    assert f(A16, 4096, A16, 4096, None, A16, 4096, 0, 4, 8, 4096, None) == 1    # null bias
+    assert f(A16, 4096, A16, 4096, A16 + 4, A16, 4096, 0, 4, 8, 4096, None) == 1  # bias misaligned
+    assert f(A16, 4096, A16, 4000, A16, A16, 4096, 0, 4, 8, 4096, None) == 1     # ldw < K

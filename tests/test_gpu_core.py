@@ -396,3 +396,24 @@ def test_mean_parity_and_batch_invariance(ops, orc, H):
         p = int(g.integers(0, B))
         xb[p] = row
         assert ops.bi_mean(dev_bf16(xb)).cpu().numpy()[p:p + 1].view(np.uint32)[0] == ref_bits, (B, p)
+
+
+# ------------------------------------------------------------------ addmm
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (37, 132, 512), (300, 1028, 1024)])
+def test_addmm_parity_and_invariance(ops, orc, M, N, K):
+    g = np.random.default_rng(M * 7 + N)
+    a = I.normal_bf16(g, (M, K))
+    w = I.normal_bf16(g, (N, K), 0, 0.05)
+    b = I.normal_bf16(g, (N,), 0, 3.0)
+    ad, wd, bd = dev_bf16(a), dev_bf16(w), dev_bf16(b)
+    got = host_bits(ops.bi_addmm(ad, wd, bd))
+    check_bf16(got, orc.addmm_f64(a, w, b), f"addmm {M}x{N}x{K}")
+    # a bias of -0.0 leaves every fp32 result unchanged: bits equal bi_matmul's
+    nz = dev_bf16(np.full(N, 0x8000, np.uint16))
+    assert np.array_equal(host_bits(ops.bi_addmm(ad, wd, nz)), host_bits(ops.bi_matmul(ad, wd)))
+    # row 0 alone equals row 0 in the batch
+    assert np.array_equal(host_bits(ops.bi_addmm(ad[:1], wd, bd)), got[:1])
+    got32 = ops.bi_addmm(ad, wd, bd, out_dtype=torch.float32).cpu().numpy()
+    ref = orc.addmm_f64(a, w, b)
+    assert np.all(np.abs(got32 - ref) <= 1e-2 * np.sqrt(np.mean(ref ** 2)))
