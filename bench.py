@@ -309,7 +309,7 @@ def main():
             "workload": "llama8b-projection sweep (RMSNorm 4096 + bf16 GEMM 4096->4096 and 4096->14336, "
                         "M=1..64,128,256,512,1024,2048) + paged decode S=256 + causal prefill 8192",
             "M_sweep": list(I.M_SWEEP), "hidden": H, "N": list(Ns),
-            "gemm_tile": "64x64x256 workgroup tile, 4 waves of 32x32, v_mfma_f32_16x16x32_bf16, 2-stage global_load_lds pipeline",
+            "gemm_tile": "64x32x128 workgroup tile, 8 waves of 16x16, v_mfma_f32_16x16x32_bf16, 3-stage global_load_lds pipeline (2 in flight)",
             "value_basis": "GEMM flops of the sweep / GPU time of the projection phase (HIP graph replay)",
             "graph_matches_eager": graph_matches_eager,
         },
