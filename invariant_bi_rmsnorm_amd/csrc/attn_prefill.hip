@@ -50,12 +50,12 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nvalid)
 }
 
 // LDS layouts of one split.  K: [256 token rows][128 dims], 16-byte chunk ch of
-// row r at slot ch ^ kswz(r) (the 16 rows of one MFMA operand read hit
-// distinct banks).  V^T: as in the cache, [16 blocks][128 dims][16 tokens], the
-// two 16-byte halves of dim row d swapped when (d >> 3) is odd (dims d and
-// d + 8 of one operand read hit distinct banks).
+// row r at slot ch ^ kswz(r).  V^T: as in the cache, [16 blocks][128 dims][16
+// tokens], unswizzled.  Both operand reads are free of bank conflicts on gfx950
+// (SQ_LDS_BANK_CONFLICT reads zero for them); swapping the two 16-byte halves
+// of every other group of 8 V^T dim rows, as a 32-bank layout would want,
+// costs 4 conflict cycles per read here.
 __device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
-__device__ __forceinline__ int vhalf(int d, int half) { return half ^ ((d >> 3) & 1); }
 
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const int32_t* __restrict__ q_start,
@@ -116,8 +116,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
             const int inst = wave + kWaves * it;
             const int row = 4 * inst + (lane >> 4);
             const int tok = i * kSplit + row;
-            const int blk = tok < L ? s_bt[tok >> 4] : -1;
-            if (blk >= 0) {
+            // the 4 rows of one load lie in one cache block: its id is wave-uniform
+            const int tb = (i * kSplit + 4 * inst) >> 4;
+            const int blk = __builtin_amdgcn_readfirstlane(tb * kBlock < L ? s_bt[tb] : -1);
+            if (blk >= 0 && tok < L) {
                 const int gch = (lane & 15) ^ kswz(row);
                 __builtin_amdgcn_global_load_lds(
                     kc + (((int64_t)blk * Hkv + g) * kBlock + (tok & 15)) * kD + gch * 8,
@@ -132,10 +134,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
             const int b = inst >> 2;
             const int d = 32 * (inst & 3) + (lane >> 1);
             const int tb = i * (kSplit / kBlock) + b;
-            const int blk = tb * kBlock < L ? s_bt[tb] : -1;
+            const int blk = __builtin_amdgcn_readfirstlane(tb * kBlock < L ? s_bt[tb] : -1);
             if (blk >= 0)
                 __builtin_amdgcn_global_load_lds(
-                    vc + (((int64_t)blk * Hkv + g) * kD + d) * kBlock + vhalf(d, lane & 1) * 8,
+                    vc + (((int64_t)blk * Hkv + g) * kD + d) * kBlock + (lane & 1) * 8,
                     s_v + inst * 512, 16, 0, 0);
         }
     };
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) {
                     const int d = 16 * dt + col;
-                    u32x4 v = ld16(s_v + b * (kD * kBlock) + d * kBlock + vhalf(d, grp & 1) * 8);
+                    u32x4 v = ld16(s_v + b * (kD * kBlock) + d * kBlock + (grp & 1) * 8);
                     if constexpr (kTail) {
                         if (tok + 8 > L) v = tok >= L ? zero_u32x4() : keep_first(v, L - tok);
                     }

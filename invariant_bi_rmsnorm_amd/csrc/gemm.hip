@@ -29,8 +29,10 @@
 //     staging), three 24 KB stages (two in flight while one is consumed),
 //     72 KB in all, so two workgroups share a CU at large M; a row's 128-wide
 //     k slice is 256 contiguous bytes in HBM;
-//   * LDS rows are 256 B with the 16-byte chunks XOR-swizzled by (row & 7),
-//     so the 16 rows an MFMA operand read touches fall in different banks;
+//   * LDS rows are 256 B with the 16-byte chunks XOR-swizzled by (row & 15):
+//     the 16 rows of an MFMA operand read then hit distinct 16-byte slots and
+//     the read has no bank conflicts on gfx950 (a (row & 7) swizzle costs 4
+//     conflict cycles per read there);
 //   * tiles are dealt to the 8 XCDs in contiguous ranges of a grouped order
 //     (bands of 4 m-tiles, n-major inside a band), so the wavefronts running
 //     together on one XCD share A and W slices in that XCD's L2;

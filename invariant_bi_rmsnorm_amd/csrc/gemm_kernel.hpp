@@ -60,7 +60,7 @@ __device__ __forceinline__ void wait_vm_upto(int n)
     }
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & (kChunks - 1)); }
 
 template <int kOrder>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
