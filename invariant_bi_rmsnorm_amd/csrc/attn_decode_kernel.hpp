@@ -11,7 +11,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxSeqs = 2048;
-constexpr int kPtStride = kSplit + 8;   // bf16 per row of the P^T buffer (16 B pad)
+// bf16 per row of the P^T buffer: a 32-byte pad makes the 16-byte operand
+// reads and writes of one wavefront free of LDS bank conflicts on gfx950
+// (a 16-byte pad costs 4 conflict cycles per access there)
+constexpr int kPtStride = kSplit + 16;
+static_assert(16 * kPtStride <= kSplit * kD, "P^T fits in the K buffer it aliases");
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 

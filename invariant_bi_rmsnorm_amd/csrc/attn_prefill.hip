@@ -162,16 +162,23 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         auto softmax_part = [&](auto masked) {
             constexpr bool kMasked = decltype(masked)::value;
             float sv[kChunks][8];
+            bf16x8 kf[2][4];             // [step parity][dc]: the next tile's K operands load while this one multiplies
+            auto load_k = [&](int st, bf16x8 (&dst)[4]) __attribute__((always_inline)) {
+                const int row = 32 * (st >> 1) + score_row_token(col, st & 1);
+#pragma unroll
+                for (int dc = 0; dc < 4; ++dc)
+                    dst[dc] = *reinterpret_cast<const bf16x8*>(s_k + row * kD + (((4 * dc + grp) ^ kswz(row)) * 8));
+            };
+            load_k(0, kf[0]);
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
 #pragma unroll
                 for (int th = 0; th < 2; ++th) {
-                    const int row = 32 * c + score_row_token(col, th);
-                    bf16x8 kf[4];
-#pragma unroll
-                    for (int dc = 0; dc < 4; ++dc)
-                        kf[dc] = *reinterpret_cast<const bf16x8*>(s_k + row * kD + (((4 * dc + grp) ^ kswz(row)) * 8));
-                    const f32x4 acc = score_tile(kf, qf);
+                    const int st = 2 * c + th;
+                    if (st + 1 < 2 * kChunks) load_k(st + 1, kf[(st + 1) & 1]);
+                    // only VALU / SALU work may be scheduled across: the loads stay ahead
+                    __builtin_amdgcn_sched_barrier(0x6);
+                    const f32x4 acc = score_tile(kf[st & 1], qf);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = 4 * th + r;
@@ -214,14 +221,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto values_part = [&](auto tail) {
             constexpr bool kTail = decltype(tail)::value;
+            u32x4 vf[2][4];              // [step parity][dt % 4]: the next half chunk's V operands load while this one multiplies
+            auto load_v = [&](int st, u32x4 (&dst)[4]) __attribute__((always_inline)) {
+                const int b = 2 * (st >> 1) + (grp >> 1);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    dst[k] = ld16(s_v + b * (kD * kBlock) + (16 * (4 * (st & 1) + k) + col) * kBlock + (grp & 1) * 8);
+            };
+            load_v(0, vf[0]);
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
                 const int tok = t0 + 32 * c + 8 * grp;
-                const int b = 2 * c + (grp >> 1);
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) {
-                    const int d = 16 * dt + col;
-                    u32x4 v = ld16(s_v + b * (kD * kBlock) + d * kBlock + (grp & 1) * 8);
+                    const int st = 2 * c + (dt >> 2);
+                    if ((dt & 3) == 0) {
+                        if (st + 1 < 2 * kChunks) load_v(st + 1, vf[(st + 1) & 1]);
+                        __builtin_amdgcn_sched_barrier(0x6);
+                    }
+                    u32x4 v = vf[st & 1][dt & 3];
                     if constexpr (kTail) {
                         if (tok + 8 > L) v = tok >= L ? zero_u32x4() : keep_first(v, L - tok);
                     }
