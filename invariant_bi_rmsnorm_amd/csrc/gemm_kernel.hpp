@@ -158,31 +158,49 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         const uint16_t* sa = smem + (kt % kStages) * (kStageA + kStageW);
         const uint16_t* sw = sa + kStageA;
         const int nks = min(kBK, K - kt * kBK) / 32;       // 32-wide k chunks in this tile
+        // operands of one 32-wide k chunk, read from LDS
+        auto read_ops = [&](int ks, bf16x8 (&fw)[kTN], bf16x8 (&fa)[kTM]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < kBK / 32; ++ks) {
-            if (ks < nks) {
-                bf16x8 fw[kTN], fa[kTM];
+            for (int i = 0; i < kTN; ++i) {
+                const int row = wn * (kBN / kWN) + 16 * i + col;
+                fw[i] = *reinterpret_cast<const bf16x8*>(sw + row * kBK + swz(row, 4 * ks + grp) * 8);
+            }
 #pragma unroll
-                for (int i = 0; i < kTN; ++i) {
-                    const int row = wn * (kBN / kWN) + 16 * i + col;
-                    fw[i] = *reinterpret_cast<const bf16x8*>(sw + row * kBK + swz(row, 4 * ks + grp) * 8);
-                }
+            for (int j = 0; j < kTM; ++j) {
+                const int row = wm * (kBM / kWM) + 16 * j + col;
+                fa[j] = *reinterpret_cast<const bf16x8*>(sa + row * kBK + swz(row, 4 * ks + grp) * 8);
+            }
+        };
+        // the chain step of one k chunk (ascending ks within the tile)
+        auto chain = [&](int ks, const bf16x8 (&fw)[kTN], const bf16x8 (&fa)[kTM]) __attribute__((always_inline)) {
 #pragma unroll
-                for (int j = 0; j < kTM; ++j) {
-                    const int row = wm * (kBM / kWM) + 16 * j + col;
-                    fa[j] = *reinterpret_cast<const bf16x8*>(sa + row * kBK + swz(row, 4 * ks + grp) * 8);
-                }
+            for (int j = 0; j < kTM; ++j) {
+                if (j < tmv) {
 #pragma unroll
-                for (int j = 0; j < kTM; ++j) {
-                    if (j < tmv) {
-#pragma unroll
-                        for (int i = 0; i < kTN; ++i) {
-                            if (kOrder == 1 && (ks & 1))
-                                acc2[i][j] = mfma16(fw[i], fa[j], acc2[i][j]);
-                            else
-                                acc[i][j] = mfma16(fw[i], fa[j], acc[i][j]);
-                        }
+                    for (int i = 0; i < kTN; ++i) {
+                        if (kOrder == 1 && (ks & 1))
+                            acc2[i][j] = mfma16(fw[i], fa[j], acc2[i][j]);
+                        else
+                            acc[i][j] = mfma16(fw[i], fa[j], acc[i][j]);
                     }
+                }
+            }
+        };
+        if (tmv > 0) {                                     // wave-uniform: rows < M in this wave's tile
+            if (nks == kBK / 32) {
+                // whole tile: every operand read is issued before the first MFMA,
+                // so the LDS latency is paid once per tile, not once per k chunk
+                bf16x8 fw[kBK / 32][kTN], fa[kBK / 32][kTM];
+#pragma unroll
+                for (int ks = 0; ks < kBK / 32; ++ks) read_ops(ks, fw[ks], fa[ks]);
+                __builtin_amdgcn_sched_barrier(0);                 // keep the reads ahead
+#pragma unroll
+                for (int ks = 0; ks < kBK / 32; ++ks) chain(ks, fw[ks], fa[ks]);
+            } else {
+                for (int ks = 0; ks < nks; ++ks) {               // K tail
+                    bf16x8 fw[kTN], fa[kTM];
+                    read_ops(ks, fw, fa);
+                    chain(ks, fw, fa);
                 }
             }
         }
