@@ -95,17 +95,24 @@ typedef struct {
     const int32_t* q_start;     /* device [S+1]                                                 */
     const int32_t* kv_lens;     /* device [S] cache length after this step's tokens             */
     const int32_t* block_table; /* device [S][max_blocks]                                       */
-    const int32_t* logit_rows;  /* device [S] row (in 0..T-1) whose logits pick the next token  */
+    const int32_t* logit_rows;  /* device [R] rows (in 0..T-1) whose logits are taken; row r < S
+                                   is the one that picks sequence r's next token                */
+    int32_t n_logit_rows;       /* R: 0 means S; S <= R <= T.  Rows past S give the logits (and
+                                   argmax) after further tokens of a chunk, e.g. every token of a
+                                   chunk that re-checks tokens proposed by another path          */
 } bi_toy_step_desc;
 
-/* Workspace bytes for steps of up to max_tokens tokens, max_seqs sequences and
- * KV lengths up to max_kv_len; 0 if the configuration is unsupported. */
+/* Workspace bytes for steps of up to max_tokens tokens, max_seqs sequences (and
+ * logit rows) and KV lengths up to max_kv_len; 0 if the configuration is
+ * unsupported. */
 size_t bi_toy_workspace_bytes(const bi_toy_config* cfg, int32_t max_tokens, int32_t max_seqs,
                               int32_t max_kv_len);
 
-/* One greedy step: writes next_ids[s] (device int32 [S]) = argmax of the fp32
- * logits of row logit_rows[s]; logits_out (device float [S][vocab]) receives
- * those logits when non-NULL.  Each row goes through the batch-invariant
+/* One greedy step: writes next_ids[r] (device int32 [R]) = argmax of the fp32
+ * logits of row logit_rows[r]; logits_out (device float [R][vocab]) receives
+ * those logits when non-NULL.  BI_ERR_INVALID_ARGUMENT when n_logit_rows is
+ * negative, below S or above T; BI_ERR_WORKSPACE_TOO_SMALL when R rows do not
+ * fit the workspace.  Each row goes through the batch-invariant
  * kernels only, so next_ids[s] does not depend on which other sequences share
  * the step or on their order.  Requires head_dim == 128, hidden % 64 == 0,
  * mlp % 64 == 0 and the constraints of the bi.h entry points it calls. */

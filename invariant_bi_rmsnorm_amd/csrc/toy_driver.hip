@@ -16,7 +16,8 @@
 // (decode kernel for the single-token sequences, prefill kernel for the
 // chunks; both give the same bits for the same row) -> O matmul -> residual ->
 // RMSNorm -> gate|up matmul -> SiLU*mul -> down matmul -> residual.
-// Then the last row of each sequence: RMSNorm -> LM head (fp32 logits) -> argmax.
+// Then the last row of each sequence (and any further rows the step asks for):
+// RMSNorm -> LM head (fp32 logits) -> argmax.
 #include "../../include/bi.h"
 #include "../../include/bi_toy.h"
 #include "bi_common.hpp"
@@ -88,7 +89,10 @@ extern "C" int bi_toy_step(const bi_toy_config* c, const bi_toy_weights* w, cons
     if (!st->ids || !st->pos || !st->slots || !st->q_start || !st->kv_lens || !st->block_table ||
         !st->logit_rows)
         return BI_ERR_INVALID_ARGUMENT;
-    const Layout L = layout(c, st->T, st->S, st->max_kv_len);
+    if (st->n_logit_rows < 0 || (st->n_logit_rows > 0 && (st->n_logit_rows < st->S || st->n_logit_rows > st->T)))
+        return BI_ERR_INVALID_ARGUMENT;
+    const int64_t R = st->n_logit_rows > 0 ? st->n_logit_rows : st->S;
+    const Layout L = layout(c, st->T, R, st->max_kv_len);
     if (ws_bytes < L.total) return BI_ERR_WORKSPACE_TOO_SMALL;
 
     const int64_t T = st->T, S = st->S, H = c->hidden, D = c->head_dim;
@@ -139,10 +143,10 @@ extern "C" int bi_toy_step(const bi_toy_config* c, const bi_toy_weights* w, cons
         CHECK(bi_matmul(act, F, lw[5], F, tmp, H, BI_BF16, T, H, F, stream));
         CHECK(bi_add(h, tmp, h, T * H, stream));
     }
-    CHECK(bi_gather_rows(h, H, T, st->logit_rows, S, H, hl, H, stream));
-    CHECK(bi_rmsnorm(hl, H, w->final_norm, xl, H, nullptr, S, H, c->eps, stream));
-    CHECK(bi_matmul(xl, H, w->lm_head, H, logits, V, BI_F32, S, V, H, stream));
-    CHECK(bi_argmax(logits, V, S, V, next_ids, stream));
+    CHECK(bi_gather_rows(h, H, T, st->logit_rows, R, H, hl, H, stream));
+    CHECK(bi_rmsnorm(hl, H, w->final_norm, xl, H, nullptr, R, H, c->eps, stream));
+    CHECK(bi_matmul(xl, H, w->lm_head, H, logits, V, BI_F32, R, V, H, stream));
+    CHECK(bi_argmax(logits, V, R, V, next_ids, stream));
     return BI_OK;
     BI_TRY_END
 }

@@ -47,7 +47,8 @@ class _Step(ctypes.Structure):
                 ("max_blocks", ctypes.c_int32),
                 ("ids", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("slots", ctypes.c_void_p),
                 ("q_start", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p),
-                ("block_table", ctypes.c_void_p), ("logit_rows", ctypes.c_void_p)]
+                ("block_table", ctypes.c_void_p), ("logit_rows", ctypes.c_void_p),
+                ("n_logit_rows", ctypes.c_int32)]
 
 
 def _dev16(bits: np.ndarray, device) -> torch.Tensor:
@@ -120,6 +121,23 @@ class ToyEngine:
         self.free = list(range(num_blocks))[::-1]
         self.num_blocks = num_blocks
 
+    @classmethod
+    def sharing(cls, other: "ToyEngine") -> "ToyEngine":
+        """An engine over the same weights, KV caches and block pool as `other`
+        (the same objects, so either engine's steps extend the same requests),
+        bound to the library current now, e.g. another build of the same ABI."""
+        e = cls.__new__(cls)
+        e.__dict__.update(other.__dict__)
+        e.L = ops.lib()
+        nbytes = int(e.L.bi_toy_workspace_bytes(ctypes.byref(e.c), e.max_tokens, e.max_seqs, e.max_kv_len))
+        if nbytes == 0:
+            raise ValueError("unsupported toy configuration")
+        e.ws = torch.empty((nbytes,), dtype=torch.uint8, device=e.device)
+        e.next_ids = torch.empty_like(other.next_ids)
+        e.logits = torch.empty_like(other.logits)
+        e.sampled = torch.empty_like(other.sampled)
+        return e
+
     # ---------------------------------------------------------------- blocks
     def _ensure_blocks(self, r: Request, new_len: int):
         need = -(-new_len // BLOCK)
@@ -133,12 +151,16 @@ class ToyEngine:
         r.blocks = []
 
     # ---------------------------------------------------------------- one step
-    def step(self, work, want_logits: bool = False, temperature: float = 0.0):
+    def step(self, work, want_logits: bool = False, temperature: float = 0.0, all_rows=()):
         """work: list of (request, n_tokens) with all decode entries (n == 1 and
         request decoding) first.  Returns next ids (numpy [S]) and optionally
         logits (numpy [S, vocab]).  temperature 0 takes the argmax; T > 0 draws
         with bi_sample, keyed by each request's seed, counter = the position of
-        the token drawn."""
+        the token drawn.  all_rows: indices s of work entries that also get the
+        argmax after every one of their tokens (greedy only); with it the
+        result has a third member, {s: numpy [n_tokens]}."""
+        if all_rows and temperature > 0.0:
+            raise ValueError("all_rows is for greedy steps")
         S = len(work)
         n_decode = 0
         while n_decode < S and work[n_decode][0].decoding and work[n_decode][1] == 1:
@@ -163,7 +185,13 @@ class ToyEngine:
             table[s, :len(bl)] = bl
             max_q = max(max_q, n)
         T = q_start[-1]
-        if T > self.max_tokens or S > self.max_seqs:
+        extra = {}                      # s -> positions (rows) of its tokens before the last
+        for s in sorted(set(all_rows)):
+            first, last = q_start[s], q_start[s + 1] - 1
+            extra[s] = list(range(first, last))
+            rows += extra[s]
+        R = len(rows)
+        if T > self.max_tokens or R > self.max_seqs:
             raise RuntimeError("step larger than the workspace")
         dev = self.device
         host = np.concatenate([np.asarray(ids, np.int32), np.concatenate(pos).astype(np.int32),
@@ -177,11 +205,11 @@ class ToyEngine:
             o += n
             return t
         d_ids, d_pos, d_slots = take(T), take(T), take(T)
-        d_qs, d_kv, d_rows = take(S + 1), take(S), take(S)
+        d_qs, d_kv, d_rows = take(S + 1), take(S), take(R)
         d_tab = take(S * self.max_blocks)
         st = _Step(T, S, n_decode, max_q, self.max_kv_len, self.max_blocks,
                    d_ids.data_ptr(), d_pos.data_ptr(), d_slots.data_ptr(), d_qs.data_ptr(),
-                   d_kv.data_ptr(), d_tab.data_ptr(), d_rows.data_ptr())
+                   d_kv.data_ptr(), d_tab.data_ptr(), d_rows.data_ptr(), R)
         stream = torch.cuda.current_stream().cuda_stream
         sampling = temperature > 0.0
         rc = self.L.bi_toy_step(ctypes.byref(self.c), ctypes.byref(self.w), ctypes.byref(st),
@@ -200,14 +228,23 @@ class ToyEngine:
                 raise ops.BiError(rc, "bi_sample")
             nxt = self.sampled[:S].cpu().numpy()
         else:
-            nxt = self.next_ids[:S].cpu().numpy()
+            allnext = self.next_ids[:R].cpu().numpy()
+            nxt = allnext[:S]
         lg = self.logits[:S].cpu().numpy() if want_logits else None
+        rows_next = {}
+        o = S
+        for s in sorted(extra):
+            n = len(extra[s])
+            rows_next[s] = np.concatenate([allnext[o:o + n], allnext[s:s + 1]])
+            o += n
         for s, (r, n) in enumerate(work):
             r.length += n
             del r.pending[:n]
             if not r.pending:                 # the step consumed the last pending token
                 r.generated.append(int(nxt[s]))
                 r.pending = [int(nxt[s])]
+        if all_rows:
+            return nxt, lg, rows_next
         return nxt, lg
 
 
@@ -238,7 +275,7 @@ def run_load_experiment(engine: ToyEngine, prompt: np.ndarray, n_runs: int, n_ne
     co_load = []
     while len(results) < n_runs:
         if g.random() < 0.02:                  # the server's load level drifts
-            cap = 1 if g.random() < 0.25 else int(g.integers(2, max_active + 1))
+            cap = 1 if g.random() < 0.25 or max_active < 2 else int(g.integers(2, max_active + 1))
         while len(active) < cap and g.random() < 0.7:
             if targets_started < n_runs and g.random() < 0.5:
                 active.append(Request(rid, prompt, n_new, target=True, seed=target_seed))
@@ -282,3 +319,155 @@ def run_load_experiment(engine: ToyEngine, prompt: np.ndarray, n_runs: int, n_ne
         engine.release(r)
     return results, {"steps": steps, "co_load_min": int(min(co_load)), "co_load_max": int(max(co_load)),
                      "co_load_mean": float(np.mean(co_load))}
+
+
+def run_verify_rollback(bi: ToyEngine, nb: ToyEngine, prompt: np.ndarray, n_runs: int, n_new: int, seed: int,
+                        k: int = 8, max_active: int = 32, max_step_tokens: int = 1024, other_prompt=(1, 512),
+                        other_new=(1, 256), chunk=(16, 512), progress=None, tokens_out: list | None = None,
+                        perturb=None):
+    """Selective determinism by verify-and-rollback (page "la température zéro
+    n'est pas déterministe", sections "Le prix d'une sortie bit à bit
+    identique" and "Déterminisme sélectif" and its comparison table): a fast
+    path that is not batch-invariant proposes tokens, the invariant path checks
+    them, and the output is rolled back to the first token the invariant path
+    disagrees with.
+
+    `bi` and `nb` share weights, KV caches and the block pool
+    (ToyEngine.sharing).  Each run of `prompt` is a target request: its prompt
+    is prefilled by `bi` in random chunks; then it alternates up to k draft
+    tokens decoded by `nb`, in the same nb steps as a random load of other
+    requests (which run on nb only), with one `bi` step that feeds the tokens
+    drafted since the last commit again, with a logit row per token: the
+    drafts are kept up to the first one bi's argmax disagrees with, bi's token
+    is taken there, and the cache length rolls back to the kept prefix (the bi
+    step rewrote those positions' K and V).  Every committed token is thus bi's
+    argmax over a cache written by bi, so each completion equals the invariant
+    engine's greedy completion whatever the drafts were.  perturb(position,
+    token) -> token, if given, replaces each draft token (a test hook that
+    forces rollbacks).  Returns (completion hashes, stats)."""
+    g = np.random.default_rng(seed)
+    V = bi.cfg["vocab"]
+    active: list[Request] = []
+    results = []
+    targets_started = 0
+    rid = 0
+    cap = int(g.integers(1, max_active + 1))
+    st = {"nb_steps": 0, "bi_steps": 0, "verifies": 0, "rollbacks": 0, "drafted": 0, "accepted": 0}
+    phase, commit = {}, {}              # target rid -> phase; -> (length, n_generated, next token)
+
+    def start_target():
+        nonlocal targets_started, rid
+        r = Request(rid, prompt, n_new, target=True)
+        phase[rid] = "prefill"
+        active.append(r)
+        targets_started += 1
+        rid += 1
+
+    while len(results) < n_runs:
+        if g.random() < 0.02:
+            cap = 1 if g.random() < 0.25 or max_active < 2 else int(g.integers(2, max_active + 1))
+        while len(active) < cap and g.random() < 0.7:
+            if targets_started < n_runs and g.random() < 0.5:
+                start_target()
+            else:
+                lp = int(g.integers(other_prompt[0], other_prompt[1] + 1))
+                active.append(Request(rid, g.integers(0, V, lp).astype(np.int32),
+                                      int(g.integers(other_new[0], other_new[1] + 1))))
+                rid += 1
+        if not any(r.target for r in active) and targets_started < n_runs and len(active) < max_active:
+            start_target()
+
+        # ---- fast path: load requests and drafting targets
+        dec = [r for r in active if (not r.target and r.decoding) or (r.target and phase[r.rid] == "draft")]
+        pre = [r for r in active if not r.target and not r.decoding]
+        g.shuffle(dec)
+        g.shuffle(pre)
+        work = [(r, 1) for r in dec]
+        budget = max_step_tokens - len(work)
+        for r in pre:
+            if budget <= 0:
+                break
+            n = min(len(r.pending), int(g.integers(chunk[0], chunk[1] + 1)), budget)
+            work.append((r, n))
+            budget -= n
+        if work:
+            nb.step(work)
+            st["nb_steps"] += 1
+            for r in dec:
+                if r.target:
+                    if perturb is not None:
+                        t = int(perturb(r.length, r.generated[-1]))
+                        r.generated[-1] = t
+                        r.pending = [t]
+                    c_len, c_gen, _ = commit[r.rid]
+                    drafted = len(r.generated) - c_gen
+                    if drafted >= k or c_gen + drafted > n_new:
+                        phase[r.rid] = "verify"
+
+        # ---- invariant path: target prompts and verifications
+        tg = [r for r in active if r.target and phase[r.rid] in ("prefill", "verify")]
+        if tg:
+            g.shuffle(tg)
+            work, ver, budget, rows_left = [], [], max_step_tokens, bi.max_seqs
+            for r in tg:                       # a verify entry of d tokens takes d logit rows
+                if phase[r.rid] == "verify":
+                    c_len, c_gen, c_next = commit[r.rid]
+                    drafts = r.generated[c_gen:]
+                    if len(drafts) > budget or len(drafts) > rows_left:
+                        continue
+                    r.length = c_len
+                    r.pending = [c_next] + drafts[:-1]
+                    ver.append((r, drafts))
+                    budget -= len(drafts)
+                    rows_left -= len(drafts)
+                else:
+                    if budget <= 0 or rows_left <= 0:
+                        continue
+                    n = min(len(r.pending), int(g.integers(chunk[0], chunk[1] + 1)), budget)
+                    work.append((r, n))
+                    budget -= n
+                    rows_left -= 1
+            entries = [(r, len(d)) for (r, d) in ver] + work
+            entries.sort(key=lambda e: not (e[0].decoding and e[1] == 1))      # decode entries first
+            if entries:
+                idx = {id(e[0]): i for i, e in enumerate(entries)}
+                vidx = [idx[id(r)] for (r, _) in ver]
+                _, _, rows = bi.step(entries, all_rows=vidx) if vidx else (*bi.step(entries), {})
+                st["bi_steps"] += 1
+                for (r, drafts) in ver:
+                    c_len, c_gen, c_next = commit[r.rid]
+                    b = rows[idx[id(r)]]               # bi's token after each fed token
+                    a = 0
+                    while a < len(drafts) - 1 and drafts[a] == int(b[a]):
+                        a += 1
+                    st["verifies"] += 1
+                    st["rollbacks"] += a < len(drafts) - 1          # a draft bi disagrees with
+                    st["drafted"] += len(drafts)
+                    st["accepted"] += a
+                    nxt = int(b[a])
+                    r.generated = r.generated[:c_gen] + drafts[:a] + [nxt]
+                    r.length = c_len + a + 1
+                    r.pending = [nxt]
+                    commit[r.rid] = (r.length, len(r.generated), nxt)
+                    phase[r.rid] = "draft"
+                for (r, n) in work:
+                    if r.decoding and phase[r.rid] == "prefill":     # the prompt is in: first token is bi's
+                        commit[r.rid] = (r.length, len(r.generated), r.generated[-1])
+                        phase[r.rid] = "draft"
+
+        for r in list(active):
+            fin = (r.target and r.rid in commit and commit[r.rid][1] >= n_new) or (not r.target and r.done)
+            if fin:
+                if r.target:
+                    toks = r.generated[:n_new]
+                    results.append(completion_hash(toks))
+                    if tokens_out is not None:
+                        tokens_out.append(list(toks))
+                    phase.pop(r.rid), commit.pop(r.rid)
+                bi.release(r)
+                active.remove(r)
+        if progress and (st["nb_steps"] + st["bi_steps"]) % 500 == 0:
+            progress(f"steps={st['nb_steps'] + st['bi_steps']} finished_runs={len(results)} active={len(active)}")
+    for r in active:
+        bi.release(r)
+    return results, st

@@ -173,6 +173,28 @@ def test_toy_entry_validation(L):
     assert L.bi_toy_step(None, None, None, None, 0, None, None, None) == 1
 
 
+def test_toy_step_logit_rows_validation(L):
+    """n_logit_rows: 0 means S; otherwise S <= R <= T, checked before anything
+    runs (fake device pointers; every call here returns on the host)."""
+    import ctypes
+    from invariant_bi_rmsnorm_amd import inputs as I
+    from invariant_bi_rmsnorm_amd.toy import _Cfg, _Step, _Weights
+    c = I.TOY
+    cfg = _Cfg(c["layers"], c["hidden"], c["heads"], c["kv_heads"], c["head_dim"], c["mlp"], c["vocab"],
+               1024, float(c["eps"]), float(c["rope_theta"]))
+    w = _Weights(A16, A16, A16, A16, A16, A16, 16, A16)
+
+    def step(R, ws_bytes=0):
+        st = _Step(4, 2, 0, 2, 16, 1, A16, A16, A16, A16, A16, A16, A16, R)
+        return L.bi_toy_step(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(st), A16, ws_bytes, A16, None, None)
+    for bad in (-1, 1, 5):                      # negative, below S, above T
+        assert step(bad) == 1, bad
+    for ok in (0, 2, 3, 4):                     # accepted, then the empty workspace is too small
+        assert step(ok) == 3, ok
+    need = L.bi_toy_workspace_bytes(ctypes.byref(cfg), 4, 4, 16)
+    assert need > L.bi_toy_workspace_bytes(ctypes.byref(cfg), 4, 2, 16) > 0
+
+
 def test_binding_shape_checks():
     """The binding refuses tensors whose shape, dtype or layout disagrees with
     what it passes to the C side (the library sees only pointers and sizes)."""

@@ -194,3 +194,77 @@ def test_toy_sampled_runs_collapse_to_one_completion(ops, toy_weights):
         f"unique completions: {len(uniq)}")
     assert len(hashes) == n_runs
     assert len(uniq) == 1
+
+
+# ------------------------------------------------------------------ verify-and-rollback (NEXT row f2)
+
+def _greedy_alone(eng, prompt, n_new):
+    """The engine's greedy completion of `prompt` with no other request, and
+    the fp32 logits row of every step."""
+    from invariant_bi_rmsnorm_amd.toy import Request
+    r = Request(0, prompt, n_new)
+    work = [(r, len(prompt))]
+    lg = []
+    while not r.done:
+        _, l = eng.step(work, want_logits=True)
+        lg.append(l[0].copy())
+        work = [(r, 1)]
+    eng.release(r)
+    return list(r.generated), lg
+
+
+def test_toy_logit_rows_of_a_chunk_equal_token_by_token_decode(ops, toy_weights):
+    """A chunk fed with a logit row per token (n_logit_rows > S) gives, bit for
+    bit, the logits and argmax that decoding the same tokens one at a time
+    gives: the invariant path can re-check k proposed tokens in one step."""
+    from invariant_bi_rmsnorm_amd.toy import Request
+    eng = make_engine(toy_weights)
+    prompt = I.toy_prompt(I.TOY, 64)
+    n = 24
+    toks, lg = _greedy_alone(eng, prompt, n)
+    r = Request(1, prompt, 10 ** 6)
+    eng.step([(r, len(prompt))])                     # the prompt; its argmax is the first token
+    assert r.generated[0] == toks[0]
+    r.pending = list(toks[:n - 1])                   # then t0 .. t(n-2) as one chunk
+    _, _, rows = eng.step([(r, n - 1)], want_logits=True, all_rows=[0])
+    R = n - 1
+    L = eng.logits[:R].cpu().numpy()
+    L = np.concatenate([L[1:], L[:1]])               # the sequence's own (last) row comes first
+    eng.release(r)
+    assert np.array_equal(rows[0], np.array(toks[1:n]))
+    assert np.array_equal(L.view(np.uint32), np.stack(lg[1:n]).view(np.uint32))
+
+
+def test_toy_verify_rollback_equals_invariant_greedy(ops, toy_weights):
+    """NEXT row f2 (verify-and-rollback): the non-invariant build drafts k
+    tokens at a time under random co-batched load, the invariant build
+    re-checks them with a logit row per token and rolls back at the first
+    disagreement.  Every completion equals the invariant engine's own greedy
+    completion: once with the drafts as they come, once with every draft at a
+    position divisible by 5 corrupted, which forces rollbacks."""
+    from invariant_bi_rmsnorm_amd.toy import ToyEngine, run_verify_rollback
+    prompt = I.toy_prompt(I.TOY, 64)
+    n_new, n_runs = 128, 40
+    bi = make_engine(toy_weights)
+    ref, _ = _greedy_alone(bi, prompt, n_new)
+    prev = ops.use_library(ops.NB_LIB_PATH)
+    try:
+        nb = ToyEngine.sharing(bi)
+    finally:
+        ops.use_library(prev)
+    V = I.TOY["vocab"]
+    cases = (("drafts as decoded", None),
+             ("every 5th position corrupted", lambda p, t: (t + 1) % V if p % 5 == 0 else t))
+    for name, perturb in cases:
+        toks = []
+        t = time.time()
+        hashes, st = run_verify_rollback(bi, nb, prompt, n_runs, n_new, seed=5010, k=8, tokens_out=toks,
+                                         perturb=perturb)
+        log(f"verify-rollback ({name}): {n_runs} runs x {n_new} tokens in {time.time() - t:.1f}s, {st}; "
+            f"{n_runs * n_new / st['verifies']:.2f} tokens committed per invariant check, "
+            f"{st['rollbacks']} of {st['verifies']} checks rolled back")
+        assert len(toks) == n_runs
+        assert all(tk == ref for tk in toks)
+        assert st["drafted"] > 0 and st["verifies"] > 0
+        if perturb is not None:
+            assert st["rollbacks"] > 0
