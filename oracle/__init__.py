@@ -60,6 +60,7 @@ def _load():
     lib.or_mean.argtypes = [P, I64, P, I64, I64]
     lib.or_philox4x32_10.argtypes = [P, P, P, I64]
     lib.or_top2.argtypes = [P, I64, I64, I64, P, P]
+    lib.or_lm_head_f64.argtypes = [P, I64, P, D, P, I64, P, I64, I64, I64, I64]
     lib.or_sample.argtypes = [P, I64, I64, I64, ctypes.c_float, P, P, P, P]
     lib.or_num_threads.restype = ctypes.c_int
     lib.or_rope.argtypes = [P, P, P, I64, I32, I32, D]
@@ -299,6 +300,21 @@ def top2(x):
     m = np.empty(rows, np.float32)
     _load().or_top2(_p(x), V, rows, V, _p(ids), _p(m))
     return ids, m
+
+
+def lm_head_f64(h, w, eps: float, wt):
+    """Output head without the bf16 rounding of the normalized hidden state:
+    h [R,H] bf16 bits (before the final norm), w [H], wt [V,H] bf16 bits ->
+    logits [R,V] float64 (page arxiv-daily-jp.pages.dev/paper/2609.26621,
+    abstract)."""
+    h = _u16(h); w = _u16(w); wt = _u16(wt)
+    R, H = h.shape
+    V, H2 = wt.shape
+    if H != H2:
+        raise ValueError("hidden sizes differ")
+    out = np.empty((R, V), dtype=np.float64)
+    _load().or_lm_head_f64(_p(h), H, _p(w), float(eps), _p(wt), H, _p(out), V, R, V, H)
+    return out
 
 
 class _ToyCfg(ctypes.Structure):

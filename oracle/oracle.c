@@ -424,6 +424,34 @@ void or_top2(const float* logits, int64_t ld, int64_t rows, int64_t V, int32_t* 
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Output head without the bf16 rounding of the normalized hidden state     */
+/* (page arxiv-daily-jp.pages.dev/paper/2609.26621, abstract: output flips   */
+/* follow from the top-2 logit margin at the LM head, and recomputing that  */
+/* head in FP32 only where the margin is small was the best low-cost fix).  */
+/* For each row r of h:  y = the unrounded RMSNorm of h_r (or_rmsnorm_f64),   */
+/*     out[r][v] = sum_j y_j * W[v][j],   j = 0 .. H-1, in double.           */
+/* ------------------------------------------------------------------------ */
+
+void or_lm_head_f64(const uint16_t* h, int64_t ldh, const uint16_t* w, double eps,
+                    const uint16_t* wt, int64_t ldw, double* out, int64_t ldo,
+                    int64_t R, int64_t V, int64_t H)
+{
+    double* y = (double*)malloc((size_t)H * sizeof(double));
+    if (!y) return;
+    for (int64_t r = 0; r < R; ++r) {
+        or_rmsnorm_f64(h + r * ldh, ldh, w, y, H, NULL, 1, H, eps);
+#pragma omp parallel for schedule(static)
+        for (int64_t v = 0; v < V; ++v) {
+            const uint16_t* wr = wt + v * ldw;
+            double s = 0.0;
+            for (int64_t j = 0; j < H; ++j) s += y[j] * bf16_bits_to_double(wr[j]);
+            out[r * ldo + v] = s;
+        }
+    }
+    free(y);
+}
+
 int or_num_threads(void)
 {
 #if defined(_OPENMP)

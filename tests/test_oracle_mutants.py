@@ -39,6 +39,9 @@ MUTANTS = {
     "gumbel_wrong_sign": ("return -log(-log(u));", "return log(-log(u));"),
     "sample_multiplies_by_temperature": ("(double)x[i] / (double)temperature", "(double)x[i] * (double)temperature"),
     "top2_second_may_be_the_top": ("if (i != best && (!have_second", "if ((!have_second"),
+    "lm_head_drops_last_term": ("for (int64_t j = 0; j < H; ++j) s += y[j] * bf16_bits_to_double(wr[j]);",
+                                "for (int64_t j = 0; j + 1 < H; ++j) s += y[j] * bf16_bits_to_double(wr[j]);"),
+    "lm_head_next_vocab_row": ("const uint16_t* wr = wt + v * ldw;", "const uint16_t* wr = wt + ((v + 1) % V) * ldw;"),
     "toy_no_final_norm": ("or_rmsnorm(h + (T - 1) * H, H, final_norm, xn, H, NULL, 1, H, c->eps);",
                           "memcpy(xn, h + (T - 1) * H, (size_t)H * 2);"),
     "toy_value_from_key_slot": ("memcpy(vv + t * Hkv * D, qkv + t * QKV + (Hq + Hkv) * D",

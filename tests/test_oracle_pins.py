@@ -523,6 +523,44 @@ def test_top2_margin_cases(orc):
     assert np.array_equal(m, (srt[:, -1] - srt[:, -2]).astype(np.float32))
 
 
+def test_lm_head_f64_one_hot_closed_form(orc):
+    """h = a e_k: mean of squares a^2/H, so every logit is
+    a / sqrt(a^2/H + eps) * w_k * W[v][k] (pins the 1/H, eps inside the root,
+    the weight and the column of W that is read; k = H-1 pins the last term)."""
+    H, V, eps = 64, 7, 1e-6
+    g = np.random.default_rng(71)
+    w = I.normal_bf16(g, (H,))
+    wt = I.normal_bf16(g, (V, H))
+    wd, wtd = orc.bf16_to_f64(w), orc.bf16_to_f64(wt)
+    for k, a_bits in ((0, 0x3FC0), (H - 1, 0xC020), (17, 0x4100)):        # 1.5, -2.5, 8.0
+        h = np.zeros((1, H), np.uint16)
+        h[0, k] = a_bits
+        a = float(orc.bf16_to_f64(np.array([a_bits], np.uint16))[0])
+        exp = a / math.sqrt(a * a / H + eps) * wd[k] * wtd[:, k]
+        got = orc.lm_head_f64(h, w, eps, wt)[0]
+        assert np.allclose(got, exp, rtol=1e-13, atol=0), k
+
+
+def test_lm_head_f64_factorised_form_and_scale_invariance(orc):
+    """The head equals rstd * (W @ (w * h)) summed in another grouping, and
+    with eps = 0 it does not change when h is scaled by 2 (exact in bf16)."""
+    g = np.random.default_rng(72)
+    R, H, V = 5, 96, 40
+    h = I.normal_bf16(g, (R, H))
+    w = I.normal_bf16(g, (H,))
+    wt = I.normal_bf16(g, (V, H))
+    hd, wd, wtd = orc.bf16_to_f64(h), orc.bf16_to_f64(w), orc.bf16_to_f64(wt)
+    got = orc.lm_head_f64(h, w, 1e-5, wt)
+    rstd = 1.0 / np.sqrt(np.mean(hd * hd, axis=1) + 1e-5)
+    exp = rstd[:, None] * ((hd * wd[None, :]) @ wtd.T)
+    scale = np.abs(hd * wd[None, :]) @ np.abs(wtd.T) * rstd[:, None]
+    assert np.all(np.abs(got - exp) <= 1e-13 * scale)
+    h2 = orc.round_bf16(2.0 * hd)
+    a = orc.lm_head_f64(h, w, 0.0, wt)
+    b = orc.lm_head_f64(h2, w, 0.0, wt)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
+
+
 # ---------------------------------------------------------------- sanity
 
 def test_float_addition_order_matters():
