@@ -247,6 +247,27 @@ int bi_top2(const float* logits, int64_t ld, int64_t rows, int64_t V, int32_t* i
             void* stream);
 
 /*
+ * Output head in fp32 for the rows whose top-2 margin is small (page
+ * arxiv-daily-jp.pages.dev/paper/2609.26621, abstract: recomputing the LM head
+ * in FP32 only where the margin falls below a threshold).  For each row r of
+ * h (bf16 [R][ldh], the hidden state before the final norm) whose margin is
+ * not >= threshold (every row when margin is NULL; a NaN margin counts as
+ * small):
+ *   rstd      = the rstd bi_rmsnorm gives for the row (same order, same bits),
+ *   y_j       = (h_j * rstd) * norm_w_j in fp32, not rounded to bf16,
+ *   out[r][v] = sum_j y_j * lm_head[v][j], fp32, one fixed order: per lane
+ *               j = 512 c + 8 lane + e ascending with fmaf, lanes combined by a
+ *               fixed xor butterfly (batch-invariant per row).
+ * Rows not selected are left untouched.  lm_head [V][ldw] bf16; out [R][ldo]
+ * fp32; margin [R] fp32 or NULL; all device pointers, h / norm_w / lm_head
+ * 16-byte aligned.  BI_ERR_UNSUPPORTED unless H % 512 == 0 and H <= 4096, or
+ * when R > 65535.  threshold must not be NaN; eps finite and >= 0.
+ */
+int bi_lm_head_f32(const void* h, int64_t ldh, const void* norm_w, float eps, const void* lm_head,
+                   int64_t ldw, float* out, int64_t ldo, int64_t R, int64_t V, int64_t H,
+                   const float* margin, float threshold, void* stream);
+
+/*
  * Greedy token choice (temperature 0 = argmax at every step; page
  * "la température zéro n'est pas déterministe", section "Le mensonge de la
  * température zéro").  ids[r] = index of the largest logit of row r, ties to

@@ -100,6 +100,9 @@ typedef struct {
     int32_t n_logit_rows;       /* R: 0 means S; S <= R <= T.  Rows past S give the logits (and
                                    argmax) after further tokens of a chunk, e.g. every token of a
                                    chunk that re-checks tokens proposed by another path          */
+    float fp32_head_margin;     /* > 0: rows whose top-2 margin (bi_top2) is below this get their
+                                   logits recomputed by bi_lm_head_f32 before the argmax; 0: off;
+                                   +inf: every row                                               */
 } bi_toy_step_desc;
 
 /* Workspace bytes for steps of up to max_tokens tokens, max_seqs sequences (and
@@ -111,8 +114,8 @@ size_t bi_toy_workspace_bytes(const bi_toy_config* cfg, int32_t max_tokens, int3
 /* One greedy step: writes next_ids[r] (device int32 [R]) = argmax of the fp32
  * logits of row logit_rows[r]; logits_out (device float [R][vocab]) receives
  * those logits when non-NULL.  BI_ERR_INVALID_ARGUMENT when n_logit_rows is
- * negative, below S or above T; BI_ERR_WORKSPACE_TOO_SMALL when R rows do not
- * fit the workspace.  Each row goes through the batch-invariant
+ * negative, below S or above T, or fp32_head_margin is negative or NaN;
+ * BI_ERR_WORKSPACE_TOO_SMALL when R rows do not fit the workspace.  Each row goes through the batch-invariant
  * kernels only, so next_ids[s] does not depend on which other sequences share
  * the step or on their order.  Requires head_dim == 128, hidden % 64 == 0,
  * mlp % 64 == 0 and the constraints of the bi.h entry points it calls. */

@@ -17,7 +17,8 @@
 // chunks; both give the same bits for the same row) -> O matmul -> residual ->
 // RMSNorm -> gate|up matmul -> SiLU*mul -> down matmul -> residual.
 // Then the last row of each sequence (and any further rows the step asks for):
-// RMSNorm -> LM head (fp32 logits) -> argmax.
+// RMSNorm -> LM head (fp32 logits) -> [rows with a small top-2 margin: the head
+// again in fp32 from the unrounded norm, when asked] -> argmax.
 #include "../../include/bi.h"
 #include "../../include/bi_toy.h"
 #include "bi_common.hpp"
@@ -29,7 +30,7 @@ constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t h, xn, qkv, attn, tmp, gu, act, hl, xl, logits, dws, total;
+    size_t h, xn, qkv, attn, tmp, gu, act, hl, xl, logits, marg, tids, dws, total;
 };
 
 Layout layout(const bi_toy_config* c, int64_t T, int64_t S, int32_t max_kv_len)
@@ -48,6 +49,8 @@ Layout layout(const bi_toy_config* c, int64_t T, int64_t S, int32_t max_kv_len)
     L.hl = o;     o += up((size_t)S * H * 2);
     L.xl = o;     o += up((size_t)S * H * 2);
     L.logits = o; o += up((size_t)S * c->vocab * 4);
+    L.marg = o;   o += up((size_t)S * 4);
+    L.tids = o;   o += up((size_t)S * 4);
     L.dws = o;    o += up(bi_attention_workspace_bytes((int32_t)S, (int32_t)Hq, (int32_t)D, max_kv_len));
     L.total = o;
     return L;
@@ -91,6 +94,7 @@ extern "C" int bi_toy_step(const bi_toy_config* c, const bi_toy_weights* w, cons
         return BI_ERR_INVALID_ARGUMENT;
     if (st->n_logit_rows < 0 || (st->n_logit_rows > 0 && (st->n_logit_rows < st->S || st->n_logit_rows > st->T)))
         return BI_ERR_INVALID_ARGUMENT;
+    if (!(st->fp32_head_margin >= 0.0f)) return BI_ERR_INVALID_ARGUMENT;      // negative or NaN
     const int64_t R = st->n_logit_rows > 0 ? st->n_logit_rows : st->S;
     const Layout L = layout(c, st->T, R, st->max_kv_len);
     if (ws_bytes < L.total) return BI_ERR_WORKSPACE_TOO_SMALL;
@@ -146,6 +150,13 @@ extern "C" int bi_toy_step(const bi_toy_config* c, const bi_toy_weights* w, cons
     CHECK(bi_gather_rows(h, H, T, st->logit_rows, R, H, hl, H, stream));
     CHECK(bi_rmsnorm(hl, H, w->final_norm, xl, H, nullptr, R, H, c->eps, stream));
     CHECK(bi_matmul(xl, H, w->lm_head, H, logits, V, BI_F32, R, V, H, stream));
+    if (st->fp32_head_margin > 0.0f) {
+        // rows with a small top-2 margin: the head again, from the unrounded norm
+        float* marg = (float*)(base + L.marg);
+        CHECK(bi_top2(logits, V, R, V, (int32_t*)(base + L.tids), marg, stream));
+        CHECK(bi_lm_head_f32(hl, H, w->final_norm, c->eps, w->lm_head, H, logits, V, R, V, H, marg,
+                             st->fp32_head_margin, stream));
+    }
     CHECK(bi_argmax(logits, V, R, V, next_ids, stream));
     return BI_OK;
     BI_TRY_END

@@ -55,6 +55,7 @@ SIGNATURES = {
     "bi_mean": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P]),
     "bi_sample": (ctypes.c_int, [_P, _I64, _I64, _I64, _F, _P, _P, _P, _P]),
     "bi_top2": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "bi_lm_head_f32": (ctypes.c_int, [_P, _I64, _P, _F, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _F, _P]),
     "bi_probe_mfma_bf16": (ctypes.c_int, [_P, _P, _P, _P]),
     "bi_probe_copy": (ctypes.c_int, [_P, _P, _I64, _P]),
     # include/bi_toy.h
@@ -393,6 +394,29 @@ def bi_top2(logits: torch.Tensor, stream=None):
     _check(lib().bi_top2(_ptr(logits), _ld(logits), rows, V, _ptr(ids), _ptr(margin), _stream(stream)),
            "bi_top2")
     return ids, margin
+
+
+def bi_lm_head_f32(h: torch.Tensor, norm_w: torch.Tensor, eps: float, lm_head: torch.Tensor,
+                   out: torch.Tensor = None, margin: torch.Tensor = None, threshold: float = 0.0,
+                   stream=None) -> torch.Tensor:
+    """fp32 logits [R, V] of h [R, H] (bf16, before the final norm) through the
+    unrounded final norm and lm_head [V, H]; with margin [R], only rows whose
+    margin is below threshold are written (the others of `out` are left)."""
+    _need(h, torch.bfloat16, "h"); _need(lm_head, torch.bfloat16, "lm_head")
+    _need_dense(norm_w, torch.bfloat16, (h.shape[1],), "norm_w")
+    R, H = h.shape
+    V, H2 = lm_head.shape
+    if H != H2:
+        raise ValueError("hidden sizes differ")
+    if out is None:
+        out = torch.empty((R, V), dtype=torch.float32, device=h.device)
+    _need_dense(out, torch.float32, (R, V), "out")
+    if margin is not None:
+        _need_dense(margin, torch.float32, (R,), "margin")
+    _check(lib().bi_lm_head_f32(_ptr(h), _ld(h), _ptr(norm_w), float(eps), _ptr(lm_head), _ld(lm_head),
+                                _ptr(out), _ld(out), R, V, H, _ptr(margin) if margin is not None else None,
+                                float(threshold), _stream(stream)), "bi_lm_head_f32")
+    return out
 
 
 def bi_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):

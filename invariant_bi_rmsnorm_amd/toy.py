@@ -48,7 +48,7 @@ class _Step(ctypes.Structure):
                 ("ids", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("slots", ctypes.c_void_p),
                 ("q_start", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("logit_rows", ctypes.c_void_p),
-                ("n_logit_rows", ctypes.c_int32)]
+                ("n_logit_rows", ctypes.c_int32), ("fp32_head_margin", ctypes.c_float)]
 
 
 def _dev16(bits: np.ndarray, device) -> torch.Tensor:
@@ -151,14 +151,18 @@ class ToyEngine:
         r.blocks = []
 
     # ---------------------------------------------------------------- one step
-    def step(self, work, want_logits: bool = False, temperature: float = 0.0, all_rows=()):
+    def step(self, work, want_logits: bool = False, temperature: float = 0.0, all_rows=(),
+             fp32_head_margin: float = 0.0):
         """work: list of (request, n_tokens) with all decode entries (n == 1 and
         request decoding) first.  Returns next ids (numpy [S]) and optionally
         logits (numpy [S, vocab]).  temperature 0 takes the argmax; T > 0 draws
         with bi_sample, keyed by each request's seed, counter = the position of
         the token drawn.  all_rows: indices s of work entries that also get the
         argmax after every one of their tokens (greedy only); with it the
-        result has a third member, {s: numpy [n_tokens]}."""
+        result has a third member, {s: numpy [n_tokens]}.  fp32_head_margin > 0
+        recomputes, in fp32 from the unrounded final norm, the logits of rows
+        whose top-2 margin is below it (bi_lm_head_f32) before the token is
+        taken."""
         if all_rows and temperature > 0.0:
             raise ValueError("all_rows is for greedy steps")
         S = len(work)
@@ -209,7 +213,7 @@ class ToyEngine:
         d_tab = take(S * self.max_blocks)
         st = _Step(T, S, n_decode, max_q, self.max_kv_len, self.max_blocks,
                    d_ids.data_ptr(), d_pos.data_ptr(), d_slots.data_ptr(), d_qs.data_ptr(),
-                   d_kv.data_ptr(), d_tab.data_ptr(), d_rows.data_ptr(), R)
+                   d_kv.data_ptr(), d_tab.data_ptr(), d_rows.data_ptr(), R, float(fp32_head_margin))
         stream = torch.cuda.current_stream().cuda_stream
         sampling = temperature > 0.0
         rc = self.L.bi_toy_step(ctypes.byref(self.c), ctypes.byref(self.w), ctypes.byref(st),
@@ -255,10 +259,13 @@ def completion_hash(tokens) -> str:
 def run_load_experiment(engine: ToyEngine, prompt: np.ndarray, n_runs: int, n_new: int, seed: int,
                         max_active: int = 64, max_step_tokens: int = 1024, other_prompt=(1, 512),
                         other_new=(1, 256), chunk=(16, 512), progress=None, temperature: float = 0.0,
-                        target_seed: int = 0x5EED, tokens_out: list | None = None):
+                        target_seed: int = 0x5EED, tokens_out: list | None = None,
+                        fp32_head_margin: float = 0.0):
     """Decode `prompt` n_runs times (n_new tokens each) inside a randomly
     varying continuous batch, greedily (temperature 0) or by seeded sampling
-    (every run of the prompt uses target_seed; other requests random seeds).
+    (every run of the prompt uses target_seed; other requests random seeds);
+    fp32_head_margin > 0 recomputes the head in fp32 for rows whose top-2
+    margin is below it (ToyEngine.step).
     Returns (list of completion hashes, stats); with tokens_out, the token lists
     of the runs are appended there too.  Each run of the prompt is one
     request; it shares every step with 0..max_active-1 other requests (other
@@ -302,7 +309,7 @@ def run_load_experiment(engine: ToyEngine, prompt: np.ndarray, n_runs: int, n_ne
             n = min(len(r.pending), int(g.integers(chunk[0], chunk[1] + 1)), budget)
             work.append((r, n))
             budget -= n
-        engine.step(work, temperature=temperature)
+        engine.step(work, temperature=temperature, fp32_head_margin=fp32_head_margin)
         steps += 1
         co_load.append(len(work) - 1)
         for r in list(active):

@@ -159,6 +159,23 @@ def test_argmax_validation(L):
     assert f(None, 100, 2, 100, A16, None) == 1
 
 
+def test_lm_head_f32_validation(L):
+    f = L.bi_lm_head_f32
+    nan = float("nan")
+
+    def call(h=A16, ldh=2048, w=A16, eps=1e-6, W=A16, ldw=2048, out=A16, ldo=100, R=2, V=100, H=2048,
+             margin=None, thr=0.1):
+        return f(h, ldh, w, eps, W, ldw, out, ldo, R, V, H, margin, thr, None)
+    assert call(R=0) == 0
+    assert call(R=-1) == 1
+    assert call(ldo=99) == 1 and call(ldh=2047) == 1 and call(ldw=1024) == 1
+    assert call(eps=-1.0) == 1 and call(eps=nan) == 1 and call(thr=nan) == 1
+    assert call(h=MIS) == 1 and call(W=None) == 1 and call(margin=MIS) == 1
+    assert call(H=2000) == 2                 # H % 512
+    assert call(ldh=8192, ldw=8192, H=8192) == 2
+    assert call(R=70000) == 2
+
+
 def test_toy_entry_validation(L):
     assert L.bi_embed(A16, 10, 64, A16, 0, A16, 64, None) == 0
     assert L.bi_embed(None, 10, 64, A16, 3, A16, 64, None) == 1
@@ -184,11 +201,13 @@ def test_toy_step_logit_rows_validation(L):
                1024, float(c["eps"]), float(c["rope_theta"]))
     w = _Weights(A16, A16, A16, A16, A16, A16, 16, A16)
 
-    def step(R, ws_bytes=0):
-        st = _Step(4, 2, 0, 2, 16, 1, A16, A16, A16, A16, A16, A16, A16, R)
+    def step(R, ws_bytes=0, margin=0.0):
+        st = _Step(4, 2, 0, 2, 16, 1, A16, A16, A16, A16, A16, A16, A16, R, margin)
         return L.bi_toy_step(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(st), A16, ws_bytes, A16, None, None)
     for bad in (-1, 1, 5):                      # negative, below S, above T
         assert step(bad) == 1, bad
+    assert step(0, margin=-0.5) == 1 and step(0, margin=float("nan")) == 1
+    assert step(0, margin=float("inf")) == 3 and step(0, margin=0.05) == 3
     for ok in (0, 2, 3, 4):                     # accepted, then the empty workspace is too small
         assert step(ok) == 3, ok
     need = L.bi_toy_workspace_bytes(ctypes.byref(cfg), 4, 4, 16)

@@ -417,3 +417,115 @@ def test_addmm_parity_and_invariance(ops, orc, M, N, K):
     got32 = ops.bi_addmm(ad, wd, bd, out_dtype=torch.float32).cpu().numpy()
     ref = orc.addmm_f64(a, w, b)
     assert np.all(np.abs(got32 - ref) <= 1e-2 * np.sqrt(np.mean(ref ** 2)))
+
+
+# ------------------------------------------------------------------ fp32 output head (NEXT row f3)
+
+def _abs_scale(orc, h, w, eps, wt):
+    """sum_j |y_j W[v][j]| per (row, v), y the unrounded normalised row."""
+    y, _ = orc.rmsnorm_f64(h, w, eps)
+    return np.abs(y) @ np.abs(orc.bf16_to_f64(wt)).T
+
+
+@pytest.mark.parametrize("R,V,H", [(3, 1000, 2048), (2, 77, 512), (1, 64, 4096), (4, 130, 1536)])
+def test_lm_head_f32_matches_oracle(ops, orc, R, V, H):
+    """Against the fp64 head, within the fp32 bound of this order: per lane at
+    most 64 fmaf steps plus 6 butterfly levels, each off by at most 2^-24 of the
+    running magnitude (< 4.2e-6 of sum_j |y_j W_vj|), and y's two products and
+    rstd a few ulp more: |out - exact| <= 1e-5 * sum_j |y_j W_vj|."""
+    g = np.random.default_rng(810 + H + V)
+    eps = 1e-5
+    h = I.normal_bf16(g, (R, H))
+    w = I.normal_bf16(g, (H,), 1.0, 0.1)
+    wt = I.normal_bf16(g, (V, H), 0.0, 0.02)
+    got = ops.bi_lm_head_f32(dev_bf16(h), dev_bf16(w), eps, dev_bf16(wt)).cpu().numpy().astype(np.float64)
+    exact = orc.lm_head_f64(h, w, eps, wt)
+    err = np.abs(got - exact) / _abs_scale(orc, h, w, eps, wt)
+    log(f"lm_head_f32 R={R} V={V} H={H}: max error {err.max():.2e} of sum|y W|")
+    assert err.max() <= 1e-5
+
+
+def test_lm_head_f32_unrounded_norm_has_rmsnorm_bits(ops):
+    """With W = the identity rows, out[r][v] = y_v exactly (one product, the
+    other fmaf steps add zero); rounding it to bf16 gives bi_rmsnorm's output
+    bits, so the head shares bi_rmsnorm's rstd and pre-rounding y bit for bit."""
+    g = np.random.default_rng(820)
+    H, R = 1024, 6
+    h = I.normal_bf16(g, (R, H), 0.0, 3.0)
+    w = I.normal_bf16(g, (H,), 1.0, 0.1)
+    eye = np.zeros((H, H), np.uint16)
+    eye[np.arange(H), np.arange(H)] = 0x3F80
+    y32 = ops.bi_lm_head_f32(dev_bf16(h), dev_bf16(w), 1e-6, dev_bf16(eye)).cpu().numpy()
+    ybf, _ = ops.bi_rmsnorm(dev_bf16(h), dev_bf16(w), 1e-6)
+    assert np.array_equal(I.f32_to_bf16(y32), host_bits(ybf))
+
+
+def test_lm_head_f32_margin_gate_and_batch_invariance(ops):
+    """Rows whose margin is >= threshold are left untouched; a row's logits do
+    not depend on which other rows share the call or on its place."""
+    g = np.random.default_rng(830)
+    R, V, H = 8, 300, 2048
+    h = I.normal_bf16(g, (R, H))
+    w = I.normal_bf16(g, (H,), 1.0, 0.1)
+    wt = I.normal_bf16(g, (V, H), 0.0, 0.02)
+    hd, wd, wtd = dev_bf16(h), dev_bf16(w), dev_bf16(wt)
+    full = ops.bi_lm_head_f32(hd, wd, 1e-5, wtd).cpu().numpy()
+    margin = torch.tensor([0.0, 1.0, 0.04, 0.05, float("nan"), 0.2, -1.0, 0.049], device="cuda")
+    out = torch.full((R, V), 123.0, device="cuda")
+    ops.bi_lm_head_f32(hd, wd, 1e-5, wtd, out=out, margin=margin, threshold=0.05)
+    out = out.cpu().numpy()
+    pick = np.array([True, False, True, False, True, False, True, True])
+    assert np.array_equal(out[pick].view(np.uint32), full[pick].view(np.uint32))
+    assert np.all(out[~pick] == 123.0)
+    perm = g.permutation(R)
+    for r in (0, 5):
+        alone = ops.bi_lm_head_f32(hd[r:r + 1], wd, 1e-5, wtd).cpu().numpy()
+        assert np.array_equal(alone[0].view(np.uint32), full[r].view(np.uint32))
+    shuf = ops.bi_lm_head_f32(hd[torch.from_numpy(perm).cuda()], wd, 1e-5, wtd).cpu().numpy()
+    assert np.array_equal(shuf.view(np.uint32), full[perm].view(np.uint32))
+
+
+def test_lm_head_f32_selective_recompute_agrees_with_exact_head(ops, orc):
+    """The measurement behind NEXT row f3, on rows shaped like the toy decoder's
+    head (hidden 2048, vocabulary 32000, W ~ N(0, 0.02)): how often the argmax of
+    the bf16 path (bi_rmsnorm, then bi_matmul with fp32 output) differs from the
+    argmax of the exact head (oracle, fp64), and how often after recomputing in
+    fp32 only the rows whose top-2 margin is below a threshold."""
+    import time
+    g = np.random.default_rng(840)
+    R, V, H, eps = 1024, 32000, 2048, 1e-5
+    h = I.normal_bf16(g, (R, H))
+    w = I.normal_bf16(g, (H,), 1.0, 0.1)
+    wt = I.normal_bf16_fast(g, (V, H))
+    wt = I.f32_to_bf16(I.bf16_to_f32(wt) * np.float32(0.02))
+    hd, wd, wtd = dev_bf16(h), dev_bf16(w), dev_bf16(wt)
+    y, _ = ops.bi_rmsnorm(hd, wd, eps)
+    lg = ops.bi_matmul(y, wtd, out_dtype=torch.float32)
+    ids, margin = ops.bi_top2(lg)
+    t = time.time()
+    exact = orc.lm_head_f64(h, w, eps, wt)
+    log(f"oracle head for {R} rows: {time.time() - t:.1f}s")
+    ex_ids = np.argmax(exact, axis=1)
+    base = int(np.sum(ids.cpu().numpy() != ex_ids))
+    m = margin.cpu().numpy()
+    res = {}
+    for thr in (0.002, 0.01, 0.05, float("inf")):
+        lg2 = lg.clone()
+        ops.bi_lm_head_f32(hd, wd, eps, wtd, out=lg2, margin=margin, threshold=thr)
+        ids2 = ops.bi_argmax(lg2).cpu().numpy()
+        res[thr] = (int(np.sum(ids2 != ex_ids)), float(np.mean(m < thr)))
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    e0, e1, e2 = E(), E(), E()
+    e0.record()
+    ops.bi_matmul(y, wtd, out_dtype=torch.float32, c=lg)
+    e1.record()
+    ops.bi_lm_head_f32(hd, wd, eps, wtd, out=lg2)
+    e2.record()
+    e2.synchronize()
+    log(f"head argmax vs the exact head over {R} rows: bf16 path {base} differ; selective fp32 "
+        + ", ".join(f"margin<{k}: {v[0]} differ ({v[1]:.1%} of rows recomputed)" for k, v in res.items())
+        + f"; time for all {R} rows: bf16 head {e0.elapsed_time(e1) * 1e3:.0f} us, "
+          f"fp32 head {e1.elapsed_time(e2) * 1e3:.0f} us")
+    assert base > 0                                  # the bf16 rounding does flip some rows
+    assert res[0.05][0] <= base // 4 and res[0.05][1] < 0.5
+    assert res[float("inf")][0] <= 1

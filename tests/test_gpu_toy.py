@@ -268,3 +268,23 @@ def test_toy_verify_rollback_equals_invariant_greedy(ops, toy_weights):
         assert st["drafted"] > 0 and st["verifies"] > 0
         if perturb is not None:
             assert st["rollbacks"] > 0
+
+
+# ------------------------------------------------------------------ selective fp32 head (NEXT row f3)
+
+def test_toy_selective_fp32_head_keeps_one_completion(ops, toy_weights):
+    """With the head recomputed in fp32 for rows whose top-2 margin is below
+    0.05, the runs under random co-batched load still give one completion (the
+    margin, the choice to recompute and the recomputation are all per row)."""
+    from invariant_bi_rmsnorm_amd.toy import run_load_experiment
+    eng = make_engine(toy_weights)
+    prompt = I.toy_prompt(I.TOY, 64)
+    base, _ = _greedy_alone(eng, prompt, 128)
+    toks = []
+    t = time.time()
+    hashes, stats = run_load_experiment(eng, prompt, 100, 128, seed=5020, tokens_out=toks, fp32_head_margin=0.05)
+    first = next((i for i, (a, b) in enumerate(zip(toks[0], base)) if a != b), None)
+    log(f"selective fp32 head (margin < 0.05): 100 runs x 128 tokens in {time.time() - t:.1f}s, {stats}, "
+        f"unique completions {len(set(hashes))}; first token that differs from the bf16-head completion: {first}")
+    assert len(hashes) == 100
+    assert len(set(hashes)) == 1
