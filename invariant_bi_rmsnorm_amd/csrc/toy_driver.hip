@@ -99,7 +99,7 @@ extern "C" int bi_toy_step(const bi_toy_config* c, const bi_toy_weights* w, cons
     const Layout L = layout(c, st->T, R, st->max_kv_len);
     if (ws_bytes < L.total) return BI_ERR_WORKSPACE_TOO_SMALL;
 
-    const int64_t T = st->T, S = st->S, H = c->hidden, D = c->head_dim;
+    const int64_t T = st->T, H = c->hidden, D = c->head_dim;
     const int32_t Hq = c->heads, Hkv = c->kv_heads;
     const int64_t F = c->mlp, V = c->vocab, QKV = (int64_t)(Hq + 2 * Hkv) * D;
     const float scale = 1.0f / sqrtf((float)D);
