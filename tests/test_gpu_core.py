@@ -485,6 +485,21 @@ def test_lm_head_f32_margin_gate_and_batch_invariance(ops):
     assert np.array_equal(shuf.view(np.uint32), full[perm].view(np.uint32))
 
 
+def test_lm_head_f32_row_strided_operands(ops):
+    """h and lm_head given as column slices of wider matrices (row strides
+    ldh, ldw > H) give the same bits as their dense copies."""
+    g = np.random.default_rng(835)
+    R, V, H = 5, 130, 1536
+    hw = dev_bf16(I.normal_bf16(g, (R, H + 72)))
+    ww = dev_bf16(I.normal_bf16(g, (V, H + 40), 0.0, 0.02))
+    w = dev_bf16(I.normal_bf16(g, (H,), 1.0, 0.1))
+    hs, ws = hw[:, 8:8 + H], ww[:, 24:24 + H]
+    assert hs.stride(0) == H + 72 and ws.stride(0) == H + 40
+    strided = ops.bi_lm_head_f32(hs, w, 1e-5, ws).cpu().numpy()
+    dense = ops.bi_lm_head_f32(hs.contiguous(), w, 1e-5, ws.contiguous()).cpu().numpy()
+    assert np.array_equal(strided.view(np.uint32), dense.view(np.uint32))
+
+
 def test_lm_head_f32_selective_recompute_agrees_with_exact_head(ops, orc):
     """The measurement behind NEXT row f3, on rows shaped like the toy decoder's
     head (hidden 2048, vocabulary 32000, W ~ N(0, 0.02)): how often the argmax of

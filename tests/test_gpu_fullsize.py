@@ -133,3 +133,29 @@ def test_prefill_full_size_chunked_sampled_parity(ops, orc):
         d = host_bits(ops.bi_attention_decode(dev_bf16(q[p][None]), kc, vc, tbl,
                                               dev_i32(np.array([p + 1], np.int32)), P, SCALE))
         assert np.array_equal(d[0], single[p]), f"decode vs prefill p={p}"
+
+
+def test_decode_largest_batch(ops, orc):
+    """S = 2048, the largest batch the decode entry point takes (its work list
+    prefix lives in LDS): short sequences drawn on the device; sampled rows
+    against the oracle and against the same sequence decoded alone, bit for
+    bit."""
+    S = 2048
+    g = np.random.default_rng([I.TAG_DECODE, 9, 0])
+    lens = g.integers(1, 300, S).astype(np.int32)
+    lens[:4] = [1, 256, 257, 299]
+    table, nblk = I.block_tables(g, lens)
+    kc, vc = device_cache(nblk, 9000)
+    poison_tails(kc, vc, table, lens)
+    q = I.queries(I.TAG_DECODE, 9, S)
+    log(f"decode S={S}: {int(lens.sum())} KV tokens")
+    out = host_bits(ops.bi_attention_decode(dev_bf16(q), kc, vc, dev_i32(table), dev_i32(lens),
+                                            int(lens.max()), SCALE))
+    for s in (0, 1, 2, 3, 1000, 2047):
+        L = int(lens[s])
+        alone = host_bits(ops.bi_attention_decode(dev_bf16(q[s][None]), kc, vc, dev_i32(table[s][None]),
+                                                  dev_i32(lens[s:s + 1]), L, SCALE))
+        assert np.array_equal(alone[0], out[s]), f"alone vs batch s={s}"
+        k, v = logical_kv(kc, vc, table[s], L)
+        _, o64 = orc.attention(q[s][None], [L - 1], k, v, SCALE)
+        check_bf16(out[s], o64[0], f"decode S=2048 s={s} L={L}", axis=None)
