@@ -54,6 +54,29 @@ def parse():
     return ap.parse_args()
 
 
+def gpu_sclk_mhz():
+    """Current shader clock of GPU 0 as rocm-smi reports it (MHz), or a note."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
+        m = re.search(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", out, re.IGNORECASE)
+        return int(m.group(1)) if m else "rocm-smi printed no sclk line"
+    except Exception as e:  # context only
+        return f"unavailable: {type(e).__name__}"
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def src_hash(*names):
     h = hashlib.sha256()
     for n in names:
@@ -238,6 +261,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    sclk_after = gpu_sclk_mhz()
     # the replayed sweep ends with M=2048: its first rows must equal the eager run bit for bit
     graph_matches_eager = bool(torch.equal(C[14336][:64].view(torch.int16), ref_c.view(torch.int16)))
     # per-launch durations of bi_matmul: eager passes of the same sweep, a HIP
@@ -312,6 +336,7 @@ def main():
             "gemm_tile": "64x32x128 workgroup tile, 8 waves of 16x16, v_mfma_f32_16x16x32_bf16, 3-stage global_load_lds pipeline (2 in flight)",
             "value_basis": "GEMM flops of the sweep / GPU time of the projection phase (HIP graph replay)",
             "graph_matches_eager": graph_matches_eager,
+            "gpu_sclk_mhz_after_timed_steps": sclk_after,
         },
         "roofline": {
             "kernel": "bi_matmul (gemm_kernel)",
@@ -464,6 +489,29 @@ def main():
                             "GB/s": round(2 * COPY_PROBE_BYTES / (copy_us * 1e-6) / 1e9, 1)}
     del src, dst
 
+    # the same sweep of GEMMs (no RMSNorm) through the invariant library and through
+    # libbi_nb.so (batch-size-dependent K order at small M), each as a HIP graph
+    def sweep_gemms():
+        for M in I.M_SWEEP:
+            for N in Ns:
+                ops.bi_matmul(y[:M], W[N][call[0] % N_WEIGHT_COPIES], c=C[N][:M])
+                call[0] += 1
+
+    try:
+        inv_us = graph_us(sweep_gemms, 1)
+        prev = ops.use_library(ops.NB_LIB_PATH)
+        try:
+            nb_us = graph_us(sweep_gemms, 1)
+        finally:
+            ops.use_library(prev)
+        result["baseline_nb_gemm_sweep"] = {
+            "invariant_TFLOP/s": round(gemm_flops_step / (inv_us * 1e-6) / 1e12, 3),
+            "nb_TFLOP/s": round(gemm_flops_step / (nb_us * 1e-6) / 1e12, 3),
+            "note": "the 138 GEMMs of the sweep as one HIP graph, invariant library vs libbi_nb.so "
+                    "(the same tile with a batch-size-dependent K order at M <= 128)"}
+    except Exception as e:  # context only
+        result["baseline_nb_gemm_sweep"] = {"error": str(e)[:200]}
+
     # non-invariant vendor GEMM (hipBLASLt through torch) on the same sweep, context only
     try:
         torch.cuda.synchronize()
@@ -498,7 +546,7 @@ def main():
         dt = time.perf_counter() - t
         fl = 2 * rows * 14336 * H
         result["cpu_baseline"] = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
-                                  "cores": oracle.num_threads(), "kind": "oracle",
+                                  "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
                                   "sample": f"oracle matmul (fp64) of {rows} rows of the M=2048 "
                                             f"[M,4096]x[4096,14336] GEMM, {dt:.1f} s"}
 
