@@ -55,15 +55,21 @@ def parse():
 
 
 def gpu_sclk_mhz():
-    """Current shader clock of GPU 0 as rocm-smi reports it (MHz), or a note."""
+    """Current shader clock (MHz) of the first amdgpu device, from the DPM level
+    sysfs marks with '*' (a file read: no child process), or a note."""
+    import glob
     import re
-    import subprocess
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
-        m = re.search(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", out, re.IGNORECASE)
-        return int(m.group(1)) if m else "rocm-smi printed no sclk line"
-    except Exception as e:  # context only
-        return f"unavailable: {type(e).__name__}"
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*Mhz", line, re.IGNORECASE)
+                        if m:
+                            return int(m.group(1))
+        except OSError:
+            continue
+    return "unavailable (no pp_dpm_sclk)"
 
 
 def cpu_model():
