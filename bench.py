@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip", default="", help="comma list of phases to skip: decode,prefill")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the supplementary points (RMSNorm 1 GiB, log_softmax, decode S sweep, prefill P sweep)")
@@ -540,21 +540,23 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         oracle.build(force=False)
+        # the oracle on the sweep's own GEMMs (every M, both N, in the sweep's
+        # order), stopped once it has run 3 x --cpu-seconds
         a = I.llama_x(2048)
-        wt = I.llama_weight(14336)
-        probe_rows = 8
-        t = time.perf_counter()
-        oracle.matmul(a[:probe_rows], wt)
+        wts = {N: I.llama_weight(N) for N in Ns}
+        fl, done, t = 0, 0, time.perf_counter()
+        for M in I.M_SWEEP:
+            for N in Ns:
+                oracle.matmul(a[:M], wts[N])
+                fl += 2 * M * N * H
+                done += 1
+            if time.perf_counter() - t > 3 * args.cpu_seconds:
+                break
         dt = time.perf_counter() - t
-        rows = int(min(2048, max(probe_rows, probe_rows * args.cpu_seconds / max(dt, 1e-3))))
-        t = time.perf_counter()
-        oracle.matmul(a[:rows], wt)
-        dt = time.perf_counter() - t
-        fl = 2 * rows * 14336 * H
         result["cpu_baseline"] = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
                                   "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
-                                  "sample": f"oracle matmul (fp64) of {rows} rows of the M=2048 "
-                                            f"[M,4096]x[4096,14336] GEMM, {dt:.1f} s"}
+                                  "sample": f"oracle matmul (fp64) of {done} of the sweep's {2 * len(I.M_SWEEP)} "
+                                            f"GEMMs ({fl / 1e9:.0f} GFLOP of {gemm_flops_step / 1e9:.0f}), {dt:.1f} s"}
 
         # the oracle beside the other rows, on bounded samples of the same work
         # (GPU times from this run: the instrumented sweep and the supplementary points)
