@@ -4,8 +4,8 @@
 One step = one pass of the hot path over one batch of synthetic input:
   1. projections (Llama-8B shapes): for every M in 1..64,128,256,...,2048:
      RMSNorm [M,4096] -> bi_matmul [M,4096]x[4096,4096] -> bi_matmul
-     [M,4096]x[4096,14336]   (weights rotated over 3 copies, 432 MB > the
-     256 MB last-level cache, so weight reads come from HBM);
+     [M,4096]x[4096,14336]   (weights rotated over 4 copies, 604 MB: more than
+     twice the 256 MB last-level cache, so weight reads come from HBM);
   2. paged decode at 256 sequences, KV lengths log-uniform in [1, 32768]
      (32/8 heads, head dim 128): bi_kv_append of the step's token + decode;
   3. causal prefill of one 8192-token prompt.
@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "invariant GEMM TFLOP/s + decode-attn HBM GB/s (% roofline), M=1..2048"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
-N_WEIGHT_COPIES = 3
+N_WEIGHT_COPIES = 4
 
 
 def parse():
