@@ -77,7 +77,7 @@ def oracle_decode(orc, q, k, v):
     return o16[0], o64[0]
 
 
-@pytest.mark.parametrize("hq,hkv", [(32, 8), (16, 4), (8, 8), (32, 2)])
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (16, 4), (8, 8), (32, 2), (16, 8), (32, 4)])
 def test_decode_parity_edge_lengths(ops, orc, hq, hkv):
     g = np.random.default_rng(hq * 10 + hkv)
     lens = np.array([1, 15, 16, 17, 255, 256, 257, 511, 1000, 2049, 4097], np.int32)
@@ -133,7 +133,8 @@ def test_decode_repeat_bitwise(ops):
 # ------------------------------------------------------------------ prefill
 
 @pytest.mark.parametrize("hq,hkv,P0,T", [(32, 8, 0, 700), (32, 8, 300, 513), (16, 4, 0, 300),
-                                         (8, 8, 1000, 77), (32, 2, 5, 260)])
+                                         (8, 8, 1000, 77), (32, 2, 5, 260), (16, 8, 40, 333),
+                                         (32, 4, 257, 129)])
 def test_prefill_parity(ops, orc, hq, hkv, P0, T):
     log(f"prefill parity Hq={hq} Hkv={hkv} P0={P0} T={T}")
     g = np.random.default_rng(P0 + T)
