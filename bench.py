@@ -4,8 +4,9 @@
 One step = one pass of the hot path over one batch of synthetic input:
   1. projections (Llama-8B shapes): for every M in 1..64,128,256,...,2048:
      RMSNorm [M,4096] -> bi_matmul [M,4096]x[4096,4096] -> bi_matmul
-     [M,4096]x[4096,14336]   (weights rotated over 4 copies, 604 MB: more than
-     twice the 256 MB last-level cache, so weight reads come from HBM);
+     [M,4096]x[4096,14336]   (each N cycles through its own 4 weight copies,
+     604 MB in all; a copy is read again only after 486 MB or more of other
+     weights, above the 256 MB last-level cache, so weight reads come from HBM);
   2. paged decode at 256 sequences, KV lengths log-uniform in [1, 32768]
      (32/8 heads, head dim 128): bi_kv_append of the step's token + decode;
   3. causal prefill of one 8192-token prompt.
@@ -39,6 +40,25 @@ METRIC = "invariant GEMM TFLOP/s + decode-attn HBM GB/s (% roofline), M=1..2048"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 N_WEIGHT_COPIES = 4
+
+
+class WeightRotation:
+    """Which copy of an N x K weight each GEMM launch reads: one counter per N,
+    so every N cycles through all of its copies whatever the launch order."""
+
+    def __init__(self, copies: int = N_WEIGHT_COPIES):
+        self.copies = copies
+        self.count = {}
+
+    def next(self, N: int) -> int:
+        k = self.count.get(N, 0)
+        self.count[N] = k + 1
+        return k % self.copies
+
+
+def sweep_schedule(m_sweep, ns, rot: WeightRotation):
+    """(M, N, copy) of every GEMM of one projection sweep, in launch order."""
+    return [(M, N, rot.next(N)) for M in m_sweep for N in ns]
 
 
 def parse():
@@ -196,7 +216,7 @@ def main():
     # ------------------------------------------------------------ one step
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     rec = {"gemm": [], "rms": [], "phase1": [], "decode": [], "prefill": []}
-    call = [0]
+    rot = WeightRotation()
 
     def phase1(record: bool):
         for M in I.M_SWEEP:
@@ -208,8 +228,7 @@ def main():
                 re_.record(stream)
                 rec["rms"].append((rs, re_, M))
             for N in Ns:
-                wt = W[N][call[0] % N_WEIGHT_COPIES]
-                call[0] += 1
+                wt = W[N][rot.next(N)]
                 if record:
                     gs, ge = E(), E()
                     gs.record(stream)
@@ -500,8 +519,7 @@ def main():
     def sweep_gemms():
         for M in I.M_SWEEP:
             for N in Ns:
-                ops.bi_matmul(y[:M], W[N][call[0] % N_WEIGHT_COPIES], c=C[N][:M])
-                call[0] += 1
+                ops.bi_matmul(y[:M], W[N][rot.next(N)], c=C[N][:M])
 
     try:
         inv_us = graph_us(sweep_gemms, 1)
@@ -526,8 +544,7 @@ def main():
             bs.record(stream)
             for M in I.M_SWEEP:
                 for N in Ns:
-                    torch.nn.functional.linear(y[:M], W[N][call[0] % N_WEIGHT_COPIES], out=C[N][:M])
-                    call[0] += 1
+                    torch.nn.functional.linear(y[:M], W[N][rot.next(N)], out=C[N][:M])
             be.record(stream)
         torch.cuda.synchronize()
         bms = bs.elapsed_time(be)
@@ -539,7 +556,7 @@ def main():
     # ------------------------------------------------------------ CPU oracle baseline
     if not args.no_cpu_baseline:
         import oracle
-        oracle.build(force=False)
+        oracle.require_built()      # built before the run; never compiled from a GPU process
         # the oracle on the sweep's own GEMMs (every M, both N, in the sweep's
         # order), stopped once it has run 3 x --cpu-seconds
         a = I.llama_x(2048)

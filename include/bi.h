@@ -151,6 +151,10 @@ size_t bi_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D, int32_t ma
  * q [S rows][ldq] bf16, row s holds Hq heads of D; out likewise with ldo.
  * block_table [S][max_blocks] int32 physical block ids; kv_lens [S] int32 in
  * [1, max_kv_len] and <= max_blocks*16.  scale multiplies q.k (1/sqrt(D) usually).
+ * A block id outside [0, num_blocks) names no block: its 16 tokens take no part
+ * in the attention (score -inf, value 0), here and in bi_attention_prefill
+ * alike, so such a row still does not depend on the rest of the batch (a row
+ * with no token left gets 0/0 = NaN).
  * ws: device workspace of at least bi_attention_workspace_bytes(S, Hq, D, max_kv_len).
  * Requires D == 128, Hq % Hkv == 0, Hq/Hkv <= 16, 1 <= max_kv_len <= 1<<20,
  * S <= 2048, 16-byte aligned q/out/caches, ldq/ldo % 8 == 0.

@@ -114,9 +114,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         }
         __syncthreads();
 
-        // a split that ends before the sequence does needs no masking (the
-        // masked code gives the same values there, with more instructions)
-        const bool whole = t0 + kSplit <= L;
+        // tokens of a block whose id is outside the pool do not exist for the
+        // arithmetic: score -inf, weight 0, value 0 (their K rows are never
+        // loaded, so nothing stale from an earlier item can reach the result)
+        bool bad = false;
+#pragma unroll
+        for (int b = 0; b < kSplit / kBlock; ++b) bad |= (t0 + kBlock * b < L) && s_blk[b] < 0;
+        // a split that ends before the sequence does and reads only valid
+        // blocks needs no masking (the masked code gives the same values
+        // there, with more instructions)
+        const bool whole = t0 + kSplit <= L && !bad;
 
         // values operands of this wave's two head-dim tiles, all 8 chunks
         // (issued first: they do not depend on the scores)
@@ -174,10 +181,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
                 for (int dc = 0; dc < 4; ++dc)
                     kf[dc] = *reinterpret_cast<const bf16x8*>(s_k + row * kD + (((4 * dc + grp) ^ kswz(row)) * 8));
                 const f32x4 acc = score_tile(kf, qf);
+                const bool blk_ok = whole || s_blk[2 * c + (grp >> 1)] >= 0;   // block of tokens 8 grp .. 8 grp + 7
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = 4 * h + r;
-                    const bool valid = whole || (t0 + 32 * c + 8 * grp + j) < L;
+                    const bool valid = whole || (blk_ok && (t0 + 32 * c + 8 * grp + j) < L);
                     sv[cc][j] = valid ? scaled_score(acc[r], scale_log2) : -INFINITY;
                 }
             }
@@ -198,10 +206,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             const int c = 2 * wave + cc;
+            const bool blk_ok = whole || s_blk[2 * c + (grp >> 1)] >= 0;
             float wv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                wv[j] = weight_f32(sv[cc][j], m, whole || (t0 + 32 * c + 8 * grp + j) < L);
+                wv[j] = weight_f32(sv[cc][j], m, whole || (blk_ok && (t0 + 32 * c + 8 * grp + j) < L));
             st16(&s_pt[col * kPtStride + 32 * c + 8 * grp], as_u32x4(pack_weights(wv)));
         }
         __syncthreads();
@@ -351,7 +360,7 @@ static inline int decode_validate(const void* q, int64_t ldq, const void* k_cach
         return BI_ERR_INVALID_ARGUMENT;
     if (Hq % Hkv) return BI_ERR_INVALID_ARGUMENT;
     if (!(scale == scale)) return BI_ERR_INVALID_ARGUMENT;
-    if (S > 0 && (!q || !k_cache || !v_cache || !block_table || !kv_lens || !out || !ws))
+    if (S > 0 && (!q || !k_cache || !v_cache || !block_table || !kv_lens || !out || !ws)))
         return BI_ERR_INVALID_ARGUMENT;
     if (ldq < (int64_t)Hq * D || ldo < (int64_t)Hq * D || (ldq % 8) || (ldo % 8))
         return BI_ERR_INVALID_ARGUMENT;

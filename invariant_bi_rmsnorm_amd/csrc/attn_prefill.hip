@@ -67,6 +67,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     __shared__ __attribute__((aligned(1024))) uint16_t s_k[kSplit * kD];     // 64 KB
     __shared__ __attribute__((aligned(1024))) uint16_t s_v[kSplit * kD];     // 64 KB
     __shared__ int s_bt[kMaxBlocks];         // physical block of every cache block the workgroup reads
+    __shared__ int s_bad[kMaxBlocks / (kSplit / kBlock)];   // split reads a block id outside the pool
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -148,12 +149,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     __syncthreads();
+    // tokens of a block whose id is outside the pool do not exist for the
+    // arithmetic (score -inf, weight 0, value 0), exactly as in decode
+    for (int sp = tid; sp < nsplit; sp += kThreads) {
+        int bad = 0;
+        for (int b = sp * (kSplit / kBlock); b < min(nblk_used, (sp + 1) * (kSplit / kBlock)); ++b)
+            bad |= s_bt[b] < 0;
+        s_bad[sp] = bad;
+    }
     issue_k(0);
 
     for (int i = 0; i < nsplit; ++i) {
         const int t0 = i * kSplit;
         __syncthreads();                 // K of split i landed; every wave is done with s_v
         issue_v(i);
+        const bool bad = s_bad[i] != 0;
         // ---------------- scores, max, weights, sum.  When every row of the
         // wavefront sees the whole split (all but the diagonal splits) the
         // causal mask is dropped: same values, fewer instructions.
@@ -179,11 +189,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
                     // only VALU / SALU work may be scheduled across: the loads stay ahead
                     __builtin_amdgcn_sched_barrier(0x6);
                     const f32x4 acc = score_tile(kf[st & 1], qf);
+                    bool blk_ok = true;
+                    if constexpr (kMasked) blk_ok = !bad || s_bt[(t0 >> 4) + 2 * c + (grp >> 1)] >= 0;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = 4 * th + r;
                         if constexpr (kMasked) {
-                            const bool valid = (t0 + 32 * c + 8 * grp + j) <= pos;
+                            const bool valid = blk_ok && (t0 + 32 * c + 8 * grp + j) <= pos;
                             sv[c][j] = valid ? scaled_score(acc[r], scale_log2) : -INFINITY;
                         } else {
                             sv[c][j] = scaled_score(acc[r], scale_log2);
@@ -198,23 +210,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
             mx = colmax_finish(mx);
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
+                bool blk_ok = true;
+                if constexpr (kMasked) blk_ok = !bad || s_bt[(t0 >> 4) + 2 * c + (grp >> 1)] >= 0;
                 float wv[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    wv[j] = weight_f32(sv[c][j], mx, kMasked ? (t0 + 32 * c + 8 * grp + j) <= pos : true);
+                    wv[j] = weight_f32(sv[c][j], mx, kMasked ? blk_ok && (t0 + 32 * c + 8 * grp + j) <= pos : true);
                 pf[c] = pack_weights(wv);
                 ls = lsum_add(ls, pf[c]);
             }
             ls = lsum_finish(ls);
         };
-        if (wave_full && t0 + kSplit - 1 <= wave_pos0)
+        if (wave_full && t0 + kSplit - 1 <= wave_pos0 && !bad)
             softmax_part(std::false_type{});
         else
             softmax_part(std::true_type{});
         __syncthreads();                 // V of split i landed; every wave is done with s_k
         if (i + 1 < nsplit) issue_k(i + 1);
         // ---------------- values.  In the split that holds the sequence end, the
-        // value slots past it are stale LDS (possibly NaN) and are zeroed; every
+        // value slots past it are stale LDS (possibly NaN) and are zeroed, as
+        // are those of blocks with an id outside the pool (never loaded); every
         // other split is whole.
         f32x4 o[8];
 #pragma unroll
@@ -242,12 +257,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
                     u32x4 v = vf[st & 1][dt & 3];
                     if constexpr (kTail) {
                         if (tok + 8 > L) v = tok >= L ? zero_u32x4() : keep_first(v, L - tok);
+                        if (bad && tok < L && s_bt[tok >> 4] < 0) v = zero_u32x4();
                     }
                     o[dt] = pv_step(as_bf16x8(v), pf[c], o[dt]);
                 }
             }
         };
-        if (t0 + kSplit <= L)
+        if (t0 + kSplit <= L && !bad)
             values_part(std::false_type{});
         else
             values_part(std::true_type{});

@@ -36,11 +36,33 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def _gpu_in_use() -> bool:
+    """True once this process has initialised the GPU through torch: from then
+    on no compiler may be started as a child process."""
+    import sys
+    torch = sys.modules.get("torch")
+    try:
+        return bool(torch is not None and torch.cuda.is_initialized())
+    except Exception:
+        return False
+
+
+def require_built() -> str:
+    """Path of liboracle.so; raises if it has not been built (it is built by
+    ``python __graft_entry__.py build`` or ``oracle.build()``, before any GPU work)."""
+    if not os.path.exists(_LIB):
+        raise RuntimeError(f"{_LIB} is not built: run `python __graft_entry__.py build` "
+                           "(or oracle.build()) before starting GPU work")
+    return _LIB
+
+
 def _load():
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB):
+        if _gpu_in_use():
+            require_built()
         build(force=False)
     lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p

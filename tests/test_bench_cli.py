@@ -60,3 +60,32 @@ def test_graft_entry_exposes_build_and_smoke():
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
     assert callable(mod.build) and callable(mod.smoke)
+
+
+def test_weight_rotation_touches_every_copy_of_each_n_and_defeats_the_llc():
+    """One projection sweep (69 M values x 2 N): each N reads all four of its
+    weight copies, in turn, and between two reads of one copy at least 256 MB
+    (the MI355X last-level cache) of other weights are read."""
+    b = _load_bench()
+    from invariant_bi_rmsnorm_amd import inputs as I
+    sched = b.sweep_schedule(I.M_SWEEP, I.LLAMA_N, b.WeightRotation())
+    assert len(sched) == 2 * len(I.M_SWEEP)
+    for N in I.LLAMA_N:
+        copies = [c for (_, n, c) in sched if n == N]
+        assert set(copies) == set(range(b.N_WEIGHT_COPIES))
+        assert all(copies[i] != copies[i + 1] for i in range(len(copies) - 1))
+    nbytes = {N: N * I.LLAMA_H * 2 for N in I.LLAMA_N}
+    last = {}
+    min_gap = None
+    for pos, (_, N, c) in enumerate(sched):
+        if (N, c) in last:
+            gap = sum(nbytes[n] for (_, n, _) in sched[last[(N, c)] + 1:pos])
+            min_gap = gap if min_gap is None else min(min_gap, gap)
+        last[(N, c)] = pos
+    assert min_gap is not None and min_gap > 256 * 10**6
+    # the rotation continues across sweeps (graph capture, eager passes, baselines)
+    rot = b.WeightRotation()
+    first = b.sweep_schedule(I.M_SWEEP, I.LLAMA_N, rot)
+    second = b.sweep_schedule(I.M_SWEEP, I.LLAMA_N, rot)
+    assert [c for (_, _, c) in second][:2] == [(len(I.M_SWEEP)) % 4] * 2
+    assert len(first) == len(second)

@@ -206,3 +206,51 @@ def test_decode_long_sequences_fold_over_chunks(ops, orc):
         assert np.array_equal(d[0], p[0])
         o16, o64 = oracle_decode(orc, q[0], k, v)
         check_bf16(d[0], o64, f"decode L={L}", axis=None)
+
+
+def test_invalid_block_ids_are_masked_in_decode_and_prefill(ops, orc):
+    """A block-table entry outside [0, num_blocks) names no cache block: its 16
+    tokens take no part in the attention (score -inf, value 0), in decode and
+    in prefill alike.  The result is the oracle's over the remaining keys, does
+    not depend on what else shares the call (nothing stale reaches it), and
+    decode at length p + 1 equals prefill row p bit for bit."""
+    g = np.random.default_rng(8)
+    L = 1000
+    k, v = I.kv_sequence(I.TAG_DECODE, 8, 0, L)
+    q = I.queries(I.TAG_DECODE, 8, L)
+    cache, table = make_cache(g, [(k, v)], extra_blocks=8)
+    nblk = cache.num_blocks
+    bad_blocks = [20] + list(range(32, 48)) + [55]        # one block, one whole split, one more
+    table = table.copy()
+    table[0, 20] = nblk + 5
+    table[0, 32:48] = nblk + 1000
+    table[0, 55] = -7
+    keep = np.ones(L, bool)
+    for b in bad_blocks:
+        keep[16 * b:16 * b + 16] = False
+    # decode of the last row: the oracle over the keys that remain
+    d_alone = decode(ops, cache, table, q[L - 1][None], np.array([L], np.int32))[0]
+    o16, o64 = oracle_decode(orc, q[L - 1], k[keep], v[keep])
+    check_bf16(d_alone, o64, "decode with invalid block ids", axis=None)
+    # the same row beside other sequences (other items run before it on the same workgroups)
+    S = 40
+    lens = I.loguniform_lengths(g, S, 6000)
+    pos = 17
+    lens[pos] = L
+    kvs = [I.kv_sequence(I.TAG_DECODE, 9, s, int(Ls)) for s, Ls in enumerate(lens)]
+    kvs[pos] = (k, v)
+    cache_b, table_b = make_cache(g, kvs)
+    tb = table_b.copy()
+    tb[pos, 20] = cache_b.num_blocks + 5
+    tb[pos, 32:48] = cache_b.num_blocks + 1000
+    tb[pos, 55] = -7
+    qb = I.queries(I.TAG_DECODE, 9, S)
+    qb[pos] = q[L - 1]
+    d_batch = decode(ops, cache_b, tb, qb, lens)
+    assert np.array_equal(d_batch[pos], d_alone)
+    # prefill over the same table: every row equals decode at its length
+    pre = prefill(ops, cache, table, q, np.array([0, L], np.int32), np.array([L], np.int32))
+    assert np.array_equal(pre[L - 1], d_alone)
+    for p in (0, 300, 319, 320, 335, 336, 511, 512, 600, 767, 768, 880, 890, 999):
+        dp = decode(ops, cache, table, q[p][None], np.array([p + 1], np.int32), max_len=L)
+        assert np.array_equal(dp[0], pre[p]), f"decode vs prefill p={p}"
