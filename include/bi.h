@@ -17,8 +17,10 @@
  *  - bf16 tensors are passed as void* to 16-bit storage (IEEE binary32 top
  *    half); fp32 as float*; indices as int32_t*.  All tensor pointers are
  *    DEVICE pointers unless stated otherwise, allocated and owned by the
- *    caller.  The library never allocates, frees or keeps device memory, and
- *    holds no mutable global state; it is safe to call from several threads.
+ *    caller.  The library never allocates or frees device memory and holds no
+ *    mutable global state, except the scratch array that
+ *    bi_attention_decode_noalloc uses instead of a caller workspace; every other
+ *    entry point is safe to call from several threads.
  *  - Leading dimensions (ld*) are in elements.  Row-major everywhere.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call is asynchronous on that stream.
@@ -164,6 +166,28 @@ int bi_attention_decode(const void* q, int64_t ldq, const void* k_cache, const v
                         const int32_t* kv_lens, void* out, int64_t ldo,
                         int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_kv_len,
                         float scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Allocation-free bi_attention_decode, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, kernels and bits as bi_attention_decode,
+ * without ws/ws_bytes: the split partials go to a scratch array that the
+ * library holds in device memory, one per GPU, until the process ends.  The
+ * call never allocates or frees memory (neither does the rest of the library).
+ * Limit: bi_attention_workspace_bytes(S, Hq, D, max_kv_len) must not exceed
+ * BI_ATTENTION_DECODE_NOALLOC_SCRATCH_BYTES (64 MiB; e.g. S * Hq *
+ * ceil(max_kv_len/256) <= 129055 for D = 128), else BI_ERR_WORKSPACE_TOO_SMALL
+ * is returned before any device work.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.  Nothing needs clearing
+ * between calls.
+ */
+#define BI_ATTENTION_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int bi_attention_decode_noalloc(const void* q, int64_t ldq, const void* k_cache, const void* v_cache,
+                                int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* kv_lens, void* out, int64_t ldo,
+                                int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_kv_len,
+                                float scale, void* stream);
 
 /*
  * Causal (chunked) prefill attention over the paged cache (same table row:

@@ -21,6 +21,8 @@
 //     ascending order and divide.
 // All arithmetic goes through attn_core.hpp, shared with the prefill kernel,
 // which is why decode at length L equals prefill row L-1 bit for bit.
+#include <mutex>
+
 #include "attn_decode_kernel.hpp"
 
 extern "C" size_t bi_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D, int32_t max_kv_len)
@@ -40,6 +42,65 @@ extern "C" int bi_attention_decode(const void* q, int64_t ldq, const void* k_cac
                                   out, ldo, S, Hq, Hkv, D, max_kv_len, scale, ws);
     if (v != BI_OK) return v < 0 ? BI_OK : v;
     if (ws_bytes < decode_ws_bytes(S, Hq, D, max_kv_len, kSplit)) return BI_ERR_WORKSPACE_TOO_SMALL;
+    return decode_launch(q, ldq, k_cache, v_cache, num_blocks, block_table, max_blocks, kv_lens, out, ldo,
+                         S, Hq, Hkv, max_kv_len, scale, ws, kSplit, stream);
+    BI_TRY_END
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant, for callers that cannot allocate device memory
+// (code under HIP graph capture, tight serving loops, harnesses that forbid
+// hipMalloc).  The split partials go to `scratch`, an array of this library in
+// device memory: each GPU the library runs on holds its own copy, at its own
+// address, until the process ends.  The array's name is a host-side stand-in:
+// host code only ever passes the address hipGetSymbolAddress returns for the
+// current device.  The partials of a call are all written by its split kernel
+// before its combine kernel reads them, so nothing has to be cleared between
+// calls; calls that overlap on one GPU share the array and race.
+constexpr size_t kNoAllocScratchBytes = BI_ATTENTION_DECODE_NOALLOC_SCRATCH_BYTES;
+constexpr int kNoAllocMaxDevices = 64;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+// Address of this device's copy of `scratch` (looked up once per device, with
+// that device current), or nullptr with *status set.
+static void* noalloc_scratch(int* status)
+{
+    static std::mutex mu;
+    static void* addr[kNoAllocMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) {
+        *status = BI_ERR_NO_DEVICE;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *status = BI_ERR_NO_DEVICE;
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+extern "C" int bi_attention_decode_noalloc(const void* q, int64_t ldq, const void* k_cache,
+                                           const void* v_cache, int64_t num_blocks,
+                                           const int32_t* block_table, int32_t max_blocks,
+                                           const int32_t* kv_lens, void* out, int64_t ldo, int32_t S,
+                                           int32_t Hq, int32_t Hkv, int32_t D, int32_t max_kv_len,
+                                           float scale, void* stream)
+{
+    BI_TRY_BEGIN
+    const int v = decode_validate(q, ldq, k_cache, v_cache, num_blocks, block_table, max_blocks, kv_lens,
+                                  out, ldo, S, Hq, Hkv, D, max_kv_len, scale, nullptr, false);
+    if (v != BI_OK) return v < 0 ? BI_OK : v;
+    // the size bound is checked on the host, before any device call
+    if (decode_ws_bytes(S, Hq, D, max_kv_len, kSplit) > kNoAllocScratchBytes) return BI_ERR_WORKSPACE_TOO_SMALL;
+    int status = BI_OK;
+    void* ws = noalloc_scratch(&status);
+    if (!ws) return status;
     return decode_launch(q, ldq, k_cache, v_cache, num_blocks, block_table, max_blocks, kv_lens, out, ldo,
                          S, Hq, Hkv, max_kv_len, scale, ws, kSplit, stream);
     BI_TRY_END

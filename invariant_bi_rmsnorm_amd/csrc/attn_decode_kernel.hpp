@@ -352,7 +352,7 @@ static inline int decode_validate(const void* q, int64_t ldq, const void* k_cach
                                   int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
                                   const int32_t* kv_lens, const void* out, int64_t ldo, int32_t S,
                                   int32_t Hq, int32_t Hkv, int32_t D, int32_t max_kv_len, float scale,
-                                  const void* ws)
+                                  const void* ws, bool caller_ws = true)
 {
     if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_blocks <= 0 || num_blocks <= 0)
         return BI_ERR_INVALID_ARGUMENT;
@@ -360,12 +360,12 @@ static inline int decode_validate(const void* q, int64_t ldq, const void* k_cach
         return BI_ERR_INVALID_ARGUMENT;
     if (Hq % Hkv) return BI_ERR_INVALID_ARGUMENT;
     if (!(scale == scale)) return BI_ERR_INVALID_ARGUMENT;
-    if (S > 0 && (!q || !k_cache || !v_cache || !block_table || !kv_lens || !out || !ws)))
+    if (S > 0 && (!q || !k_cache || !v_cache || !block_table || !kv_lens || !out || (caller_ws && !ws)))
         return BI_ERR_INVALID_ARGUMENT;
     if (ldq < (int64_t)Hq * D || ldo < (int64_t)Hq * D || (ldq % 8) || (ldo % 8))
         return BI_ERR_INVALID_ARGUMENT;
     if (S > 0 && (!bi_aligned(q, 16) || !bi_aligned(k_cache, 16) || !bi_aligned(v_cache, 16) ||
-                  !bi_aligned(out, 2) || !bi_aligned(ws, 16) || !bi_aligned(block_table, 4) ||
+                  !bi_aligned(out, 2) || (caller_ws && !bi_aligned(ws, 16)) || !bi_aligned(block_table, 4) ||
                   !bi_aligned(kv_lens, 4)))
         return BI_ERR_INVALID_ARGUMENT;
     if (D != kD || Hq / Hkv > 16 || S > kMaxSeqs || max_kv_len > (1 << 20) || Hkv > 65535)

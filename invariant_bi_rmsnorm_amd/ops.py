@@ -48,6 +48,8 @@ SIGNATURES = {
     "bi_attention_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "bi_attention_decode": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _I32, _P, _P, _I64,
                                            _I32, _I32, _I32, _I32, _I32, _F, _P, _SZ, _P]),
+    "bi_attention_decode_noalloc": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _I32, _P, _P, _I64,
+                                                   _I32, _I32, _I32, _I32, _I32, _F, _P]),
     "bi_attention_prefill": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _P, _I32, _P, _I64,
                                             _I32, _I64, _I32, _I32, _I32, _I32, _F, _P]),
     "bi_argmax": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
@@ -69,6 +71,11 @@ SIGNATURES = {
     "bi_toy_step": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P, _P, _P]),
 }
 
+# entry points the non-invariant baseline build (libbi_nb.so) does not export
+OPTIONAL_IN_BASELINE = {"bi_attention_decode_noalloc"}
+# bi_attention_decode_noalloc's limit on bi_attention_workspace_bytes (include/bi.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
 _lib = None
 
 
@@ -88,6 +95,8 @@ def lib():
                 "`python -m invariant_bi_rmsnorm_amd._build` (there is no fallback path)")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
+            if name in OPTIONAL_IN_BASELINE and not hasattr(L, name):
+                continue
             f = getattr(L, name)
             f.restype = res
             f.argtypes = args
@@ -304,6 +313,31 @@ def bi_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
                                      int(max_kv_len), float(scale), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)),
            "bi_attention_decode")
+    return out
+
+
+def bi_attention_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_table: torch.Tensor, kv_lens: torch.Tensor, max_kv_len: int,
+                                scale: float, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """bi_attention_decode without a workspace argument (the library's own
+    scratch holds the split partials); `out` [S, Hq, D] must be passed, so the
+    call allocates nothing."""
+    S = q.shape[0]
+    Hq, D, ldq = _heads_view(q, "q")
+    Hkv = k_cache.shape[1]
+    _check_paged(k_cache, v_cache, block_table, D)
+    _need_dense(block_table, torch.int32, (S, None), "block_table")
+    _need_dense(kv_lens, torch.int32, (S,), "kv_lens")
+    _, _, ldo = _heads_view(out, "out")
+    if tuple(out.shape) != (S, Hq, D):
+        raise ValueError(f"out must have shape {(S, Hq, D)}")
+    L = lib()
+    if not hasattr(L, "bi_attention_decode_noalloc"):
+        raise RuntimeError(f"bi_attention_decode_noalloc is not exported by {LIB_PATH}")
+    _check(L.bi_attention_decode_noalloc(_ptr(q), ldq, _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
+                                         _ptr(block_table), block_table.shape[1], _ptr(kv_lens), _ptr(out),
+                                         ldo, S, Hq, Hkv, D, int(max_kv_len), float(scale), _stream(stream)),
+           "bi_attention_decode_noalloc")
     return out
 
 

@@ -146,6 +146,32 @@ def test_attention_validation(L):
     assert pre(*bad) == 2                                     # block table wider than 4096
 
 
+def test_attention_decode_noalloc_validation(L):
+    """The allocation-free decode rejects, on the host and before any device
+    call, what bi_attention_decode rejects, plus any call whose split partials
+    would not fit the library's 64 MiB scratch."""
+    from invariant_bi_rmsnorm_amd import ops
+    f = L.bi_attention_decode_noalloc
+    args = [A16, 4096, A16, A16, 100, A16, 2048, A16, A16, 4096, 4, 32, 8, 128, 1000, 0.088, None]
+    bad = list(args); bad[12] = 6
+    assert f(*bad) == 1                                       # Hq % Hkv
+    bad = list(args); bad[13] = 64
+    assert f(*bad) == 2                                       # D != 128
+    bad = list(args); bad[0] = None
+    assert f(*bad) == 1                                       # null q
+    bad = list(args); bad[10] = 0
+    assert f(*bad) == 0                                       # S == 0: no-op
+    # the limit: S * Hq * ceil(max_kv_len / 256) partials of 130 floats <= 64 MiB
+    assert ops.NOALLOC_SCRATCH_BYTES == 64 << 20
+    limit_splits = ops.NOALLOC_SCRATCH_BYTES // (130 * 4)
+    assert limit_splits == 129055
+    big = list(args); big[10] = 256; big[14] = 32768          # 256 * 32 * 128 splits
+    assert L.bi_attention_workspace_bytes(256, 32, 128, 32768) > ops.NOALLOC_SCRATCH_BYTES
+    assert f(*big) == 3                                       # BI_ERR_WORKSPACE_TOO_SMALL
+    edge = list(args); edge[10] = 63; edge[14] = 2048 * 16    # 63 * 32 * 128 = 258048 splits: too many
+    assert f(*edge) == 3
+
+
 def test_probe_copy_validation(L):
     assert L.bi_probe_copy(A16, A16, 0, None) == 0
     assert L.bi_probe_copy(A16, A16, 17, None) == 1
