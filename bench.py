@@ -358,7 +358,7 @@ def main():
             "workload": "llama8b-projection sweep (RMSNorm 4096 + bf16 GEMM 4096->4096 and 4096->14336, "
                         "M=1..64,128,256,512,1024,2048) + paged decode S=256 + causal prefill 8192",
             "M_sweep": list(I.M_SWEEP), "hidden": H, "N": list(Ns),
-            "gemm_tile": "64x32x128 workgroup tile, 8 waves of 16x16, v_mfma_f32_16x16x32_bf16, 3-stage global_load_lds pipeline (2 in flight)",
+            "gemm_tile": "128x64x128 workgroup tile, 8 waves of 32x32 (2x2 MFMA tiles), v_mfma_f32_16x16x32_bf16, 3-stage global_load_lds pipeline, next k tile read from LDS during the current MFMAs",
             "value_basis": "GEMM flops of the sweep / GPU time of the projection phase (HIP graph replay)",
             "graph_matches_eager": graph_matches_eager,
             "gpu_sclk_mhz_after_timed_steps": sclk_after,
@@ -532,7 +532,7 @@ def main():
             "invariant_TFLOP/s": round(gemm_flops_step / (inv_us * 1e-6) / 1e12, 3),
             "nb_TFLOP/s": round(gemm_flops_step / (nb_us * 1e-6) / 1e12, 3),
             "note": "the 138 GEMMs of the sweep as one HIP graph, invariant library vs libbi_nb.so "
-                    "(the same tile with a batch-size-dependent K order at M <= 128)"}
+                    "(shape-tuned: split-K at M <= 64, a 128x128 tile where it fills the chip)"}
     except Exception as e:  # context only
         result["baseline_nb_gemm_sweep"] = {"error": str(e)[:200]}
 

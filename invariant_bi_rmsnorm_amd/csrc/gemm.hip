@@ -17,28 +17,30 @@
 // place in the grid or the row's place in the tile.  No split-K, no stream-K,
 // no shape-dependent dispatch.
 //
-// The one configuration (chosen by measuring the whole M = 1..2048 sweep of
-// Llama-8B projections on MI355X; small M is weight-streaming, large M is
-// MFMA/L2 bound, and one tile has to serve both):
-//   * workgroup tile 64 (m) x 32 (n) x 128 (k), 512 threads = 8 wavefronts in
-//     a 4 (m) x 2 (n) arrangement, each wavefront one 16x16 MFMA tile; small
-//     N-tiles give the weight-streaming small-M shapes more workgroups (a
-//     CU streams from HBM at a bounded rate, so the number of CUs at work is
-//     what sets their speed: N = 4096 gives 128 workgroups);
-//   * operands go global -> LDS with global_load_lds_dwordx4 (no register
-//     staging), three 24 KB stages (two in flight while one is consumed),
-//     72 KB in all, so two workgroups share a CU at large M; a row's 128-wide
-//     k slice is 256 contiguous bytes in HBM;
+// The one configuration (BiTile in gemm_kernel.hpp), chosen by timing the
+// whole M = 1..2048 sweep of Llama-8B projections (N = 4096 and 14336,
+// K = 4096) on MI355X against a dozen tiles with the same chain:
+//   * workgroup tile 128 (m) x 64 (n) x 128 (k), 512 threads = 8 wavefronts
+//     in a 4 (m) x 2 (n) arrangement, each wavefront a 32 x 32 tile of four
+//     16 x 16 MFMA tiles that share their operand reads (one 16-byte LDS read
+//     per MFMA).  Large M is bound by what the L2 delivers into the CUs'
+//     LDS, so the tile's flops per byte loaded (2 BM BN / (2 (BM + BN)) =
+//     43 flop/B) set its speed; small M streams W, and 64-wide n tiles still
+//     give N = 4096 sixty-four workgroups to stream it with;
+//   * operands go global -> LDS with global_load_lds_dwordx4, three 48 KB
+//     stages (144 KB, one workgroup per CU);
+//   * the operands of k tile kt+1 are read from LDS while the MFMAs of k tile
+//     kt run (two register sets), so the LDS latency is off the critical path;
+//   * a tile wholly inside M, N and a whole number of k tiles runs a loop with
+//     no guards and fixed wait counts; edge tiles run the same chain with
+//     wave-uniform guards (rows out of range are neither loaded nor stored,
+//     and MFMAs of 16-row groups entirely past M are skipped);
 //   * LDS rows are 256 B with the 16-byte chunks XOR-swizzled by (row & 15):
-//     the 16 rows of an MFMA operand read then hit distinct 16-byte slots and
-//     the read has no bank conflicts on gfx950 (a (row & 7) swizzle costs 4
-//     conflict cycles per read there);
+//     the 16 rows of an MFMA operand read hit distinct 16-byte slots, no bank
+//     conflicts on gfx950;
 //   * tiles are dealt to the 8 XCDs in contiguous ranges of a grouped order
-//     (bands of 4 m-tiles, n-major inside a band), so the wavefronts running
-//     together on one XCD share A and W slices in that XCD's L2;
-//   * MFMAs of 16-row groups that lie entirely at m >= M are skipped (those
-//     rows are never stored; every stored row runs the full chain).
-// M and N tails: out-of-range rows are not loaded and not stored.
+//     (bands of 4 m tiles, n-major inside a band).
+// No split-K, no stream-K, no shape-dependent choice of tile, MFMA or k order.
 #include "gemm_kernel.hpp"
 
 extern "C" int bi_matmul(const void* a, int64_t lda, const void* wt, int64_t ldw, void* c,
@@ -47,7 +49,7 @@ extern "C" int bi_matmul(const void* a, int64_t lda, const void* wt, int64_t ldw
     BI_TRY_BEGIN
     const int v = gemm_validate(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K);
     if (v != BI_OK) return v < 0 ? BI_OK : v;
-    return gemm_launch<0>(a, lda, wt, ldw, nullptr, c, ldc, c_dtype, M, N, K, stream);
+    return gemm_launch<BiTile>(a, lda, wt, ldw, nullptr, c, ldc, c_dtype, M, N, K, stream);
     BI_TRY_END
 }
 
@@ -60,6 +62,6 @@ extern "C" int bi_addmm(const void* a, int64_t lda, const void* wt, int64_t ldw,
     const int v = gemm_validate(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K);
     if (v != BI_OK) return v < 0 ? BI_OK : v;
     if (!bias || !bi_aligned(bias, 8)) return BI_ERR_INVALID_ARGUMENT;
-    return gemm_launch<0>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    return gemm_launch<BiTile>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     BI_TRY_END
 }

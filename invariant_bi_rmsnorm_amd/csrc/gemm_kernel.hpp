@@ -1,223 +1,353 @@
-// gemm_kernel.hpp -- the one GEMM kernel of the library (see gemm.hip for the
-// configuration and the invariance argument).  Template parameter kOrder
-// selects the per-element reduction order: 0 is the library's fixed chain
-// (the only order bi_matmul in libbi.so ever uses); 1 splits the chain into
-// even and odd k chunks summed at the end, an order used only by the
-// non-invariant baseline library to reproduce a batch-size-dependent switch.
+// gemm_kernel.hpp -- the GEMM kernel template.  libbi.so instantiates exactly
+// one tile configuration, BiTile below, for every bi_matmul / bi_addmm call
+// (gemm.hip states the configuration and the invariance argument).  The
+// non-invariant baseline library reuses the template with other tiles and a
+// split-K mode to build a shape-tuned comparison; nothing in libbi.so does.
+//
+// Per-element reduction order, identical for every tile of the template:
+// an fp32 accumulator starts at 0; one v_mfma_f32_16x16x32_bf16 per 32-wide k
+// chunk, chunks in ascending k; inside a chunk lane group g supplies
+// k = 8g..8g+7; W is the MFMA's A operand (rows = n), A its B operand
+// (columns = m).  An MFMA result element depends only on its own row and
+// column operands, so the bits of c[m][n] do not depend on the tile, on where
+// the tile sits in the grid or on where the row sits in the tile.
 #pragma once
+#include <type_traits>
+
 #include "bi_common.hpp"
 
 namespace {
 
-constexpr int kBM = 64;
-constexpr int kBN = 32;
-constexpr int kBK = 128;
-constexpr int kWM = 4;
-constexpr int kWN = 2;
-constexpr int kStages = 3;
-constexpr int kGroup = 4;                         // m-tiles per band of the tile order
-constexpr int kWaves = kWM * kWN;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kChunks = kBK / 8;                  // 16-byte chunks per row per k-tile
-constexpr int kRowsPerInst = 64 / kChunks;        // rows covered by one 1 KB wave load
-constexpr int kAPer = kBM / kRowsPerInst / kWaves;
-constexpr int kWPer = kBN / kRowsPerInst / kWaves;
-constexpr int kStageA = kBM * kBK;                // bf16 elements
-constexpr int kStageW = kBN * kBK;
-constexpr int kTM = kBM / kWM / 16;
-constexpr int kTN = kBN / kWN / 16;
-static_assert(kAPer * kRowsPerInst * kWaves == kBM && kWPer * kRowsPerInst * kWaves == kBN, "load split");
-
-// vmcnt <= N and lgkmcnt == 0 (expcnt unconstrained)
+// s_waitcnt vmcnt(<= N) lgkmcnt(0), expcnt unconstrained
 template <int N>
-__device__ __forceinline__ void wait_vm()
+__device__ __forceinline__ void gemm_wait_vm()
 {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
     constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
     __builtin_amdgcn_s_waitcnt(imm);
 }
 
-__device__ __forceinline__ void wait_vm_upto(int n)
+// the same with a run-time (wave-uniform) count, 0..32
+__device__ __forceinline__ void gemm_wait_vm_upto(int n)
 {
-    static_assert(kAPer + kWPer <= 16, "wait table");
     switch (n) {
-        case 0: wait_vm<0>(); break;
-        case 1: wait_vm<1>(); break;
-        case 2: wait_vm<2>(); break;
-        case 3: wait_vm<3>(); break;
-        case 4: wait_vm<4>(); break;
-        case 5: wait_vm<5>(); break;
-        case 6: wait_vm<6>(); break;
-        case 7: wait_vm<7>(); break;
-        case 8: wait_vm<8>(); break;
-        case 9: wait_vm<9>(); break;
-        case 10: wait_vm<10>(); break;
-        case 11: wait_vm<11>(); break;
-        case 12: wait_vm<12>(); break;
-        case 13: wait_vm<13>(); break;
-        case 14: wait_vm<14>(); break;
-        case 15: wait_vm<15>(); break;
-        default: wait_vm<16>(); break;
+#define GEMM_WAIT_CASE(i) case i: gemm_wait_vm<i>(); break;
+        GEMM_WAIT_CASE(0) GEMM_WAIT_CASE(1) GEMM_WAIT_CASE(2) GEMM_WAIT_CASE(3) GEMM_WAIT_CASE(4)
+        GEMM_WAIT_CASE(5) GEMM_WAIT_CASE(6) GEMM_WAIT_CASE(7) GEMM_WAIT_CASE(8) GEMM_WAIT_CASE(9)
+        GEMM_WAIT_CASE(10) GEMM_WAIT_CASE(11) GEMM_WAIT_CASE(12) GEMM_WAIT_CASE(13) GEMM_WAIT_CASE(14)
+        GEMM_WAIT_CASE(15) GEMM_WAIT_CASE(16) GEMM_WAIT_CASE(17) GEMM_WAIT_CASE(18) GEMM_WAIT_CASE(19)
+        GEMM_WAIT_CASE(20) GEMM_WAIT_CASE(21) GEMM_WAIT_CASE(22) GEMM_WAIT_CASE(23) GEMM_WAIT_CASE(24)
+        GEMM_WAIT_CASE(25) GEMM_WAIT_CASE(26) GEMM_WAIT_CASE(27) GEMM_WAIT_CASE(28) GEMM_WAIT_CASE(29)
+        GEMM_WAIT_CASE(30) GEMM_WAIT_CASE(31)
+#undef GEMM_WAIT_CASE
+        default: gemm_wait_vm<32>(); break;
     }
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & (kChunks - 1)); }
+// s_waitcnt lgkmcnt(0) only: this wave's LDS reads have returned
+__device__ __forceinline__ void gemm_wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
-template <int kOrder>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
-    const uint16_t* __restrict__ a, int64_t lda, const uint16_t* __restrict__ wt, int64_t ldw,
-    const uint16_t* __restrict__ bias, void* __restrict__ c, int64_t ldc, int c_f32, int M, int N, int K)
+// workgroup barrier without a memory fence (a fence would also wait for the
+// loads still in flight for later stages)
+__device__ __forceinline__ void gemm_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// one wavefront-wide 1 KB load: 16 bytes per lane, global -> LDS (the LDS
+// destination is the wave's base address; lane l lands at byte 16 l)
+__device__ __forceinline__ void gemm_load_lds16(const uint16_t* g, uint16_t* l)
 {
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * (kStageA + kStageW)];
+    __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+struct GemmTile {
+    static constexpr int kBM = BM, kBN = BN, kBK = BK, kWM = WM, kWN = WN, kStages = STAGES;
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kChunks = BK / 8;              // 16-byte chunks per row of a k tile
+    static constexpr int kRowsPerLoad = 64 / kChunks;   // rows one 1 KB wave load covers
+    static constexpr int kALoads = BM / kRowsPerLoad;   // wave loads per stage, A and W
+    static constexpr int kWLoads = BN / kRowsPerLoad;
+    static constexpr int kAPer = kALoads / kWaves;      // ... per wavefront
+    static constexpr int kWPer = kWLoads / kWaves;
+    static constexpr int kPer = kAPer + kWPer;
+    static constexpr int kStageA = BM * BK;             // bf16 elements per stage
+    static constexpr int kStageW = BN * BK;
+    static constexpr int kStage = kStageA + kStageW;
+    static constexpr int kWRows = BM / WM;              // rows (m) of a wavefront's tile
+    static constexpr int kWCols = BN / WN;              // columns (n) of a wavefront's tile
+    static constexpr int kTM = kWRows / 16;             // 16 x 16 MFMA tiles per wavefront
+    static constexpr int kTN = kWCols / 16;
+    static constexpr int kKS = BK / 32;                 // 32-wide k chunks per k tile
+    static constexpr int kLdsElems = STAGES * kStage;
+    static_assert(kChunks == 8 || kChunks == 16, "k tile of 64 or 128");
+    static_assert(kALoads % kWaves == 0 && kWLoads % kWaves == 0, "every wavefront issues the same loads");
+    static_assert(kTM >= 1 && kTN >= 1 && kWRows % 16 == 0 && kWCols % 16 == 0, "wavefront tile");
+    static_assert(STAGES >= 3, "one stage being read, at least one in flight, one being refilled");
+    static_assert(kLdsElems * 2 <= 160 * 1024, "LDS of one CU");
+    // LDS slot of 16-byte chunk c of row r (an involution).  The 16 rows one
+    // MFMA operand read touches land in 16 distinct 16-byte slots of a 256-byte
+    // bank row, so the reads are free of bank conflicts on gfx950.
+    __device__ static __forceinline__ int slot(int row, int c)
+    {
+        return kChunks == 16 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7));
+    }
+};
+
+// The library's one configuration (see gemm.hip for why this one).
+using BiTile = GemmTile<128, 64, 128, 4, 2, 3>;
+constexpr int kGemmGroup = 4;          // m tiles per band of the tile order
+
+// kSplitK (baseline library only): blockIdx.y = z computes the partial product
+// over k in [z K, z K + K) of operands whose rows are longer than K, into the
+// fp32 array c + z * c_split_stride.
+template <class T, bool kSplitK>
+__global__ __launch_bounds__(T::kThreads) void gemm_kernel(
+    const uint16_t* __restrict__ a, int64_t lda, const uint16_t* __restrict__ wt, int64_t ldw,
+    const uint16_t* __restrict__ bias, void* __restrict__ c, int64_t ldc, int c_f32, int M, int N, int K,
+    int64_t c_split_stride)
+{
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[T::kLdsElems];
+    constexpr int BM = T::kBM, BN = T::kBN, BK = T::kBK, S = T::kStages, KS = T::kKS;
+    constexpr int TM = T::kTM, TN = T::kTN;
+
+    if (kSplitK) {
+        a += (int64_t)blockIdx.y * K;
+        wt += (int64_t)blockIdx.y * K;
+        c = (float*)c + (int64_t)blockIdx.y * c_split_stride;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave % kWM;
-    const int wn = wave / kWM;
+    const int wm = wave % T::kWM;
+    const int wn = wave / T::kWM;
     const int col = lane & 15;
     const int grp = lane >> 4;
 
-    // ---- tile of this workgroup: XCD-contiguous ranges of a grouped order
-    const int mt = (M + kBM - 1) / kBM;
-    const int ntl = (N + kBN - 1) / kBN;
+    // ---- this workgroup's tile: the tiles in bands of kGemmGroup m tiles,
+    // n-major inside a band; the XCDs take contiguous ranges of that order
+    // (blocks are dealt to the 8 XCDs round-robin), so the workgroups running
+    // together on one XCD share A rows and W rows in that XCD's L2
+    const int mt = (M + BM - 1) / BM;
+    const int ntl = (N + BN - 1) / BN;
     const int total = mt * ntl;
     const int per_xcd = (total + 7) / 8;
     const int t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
     if (t >= total) return;
-    const int band = t / (kGroup * ntl);
-    const int gm = min(kGroup, mt - band * kGroup);
-    const int idx = t - band * kGroup * ntl;
-    const int m0 = (band * kGroup + idx % gm) * kBM;
-    const int n0 = (idx / gm) * kBN;
+    const int band = t / (kGemmGroup * ntl);
+    const int gm = min(kGemmGroup, mt - band * kGemmGroup);
+    const int idx = t - band * kGemmGroup * ntl;
+    const int m0 = (band * kGemmGroup + idx % gm) * BM;
+    const int n0 = (idx / gm) * BN;
 
-    const int lrow = lane / kChunks;
-    const int lch = lane % kChunks;
-    const int KT = (K + kBK - 1) / kBK;
+    const int lrow = lane / T::kChunks;      // row within a wave load
+    const int lch = lane % T::kChunks;       // LDS slot this lane fills
+    const int KT = (K + BK - 1) / BK;
+    const int wrow0 = m0 + wm * T::kWRows;
+    // 16-row groups of this wavefront holding at least one row < M
+    const int tmv = max(0, min(TM, (M - wrow0 + 15) / 16));
 
-    auto issue = [&](int kt, int slot) {
-        uint16_t* sa = smem + slot * (kStageA + kStageW);
-        uint16_t* sw = sa + kStageA;
-        const int kbase = kt * kBK;
+    f32x4 acc[TN][TM];
 #pragma unroll
-        for (int i = 0; i < kAPer; ++i) {
-            const int inst = wave + kWaves * i;
-            if (m0 + inst * kRowsPerInst < M) {                 // wave-uniform
-                const int row = inst * kRowsPerInst + lrow;
-                const int gch = swz(row, lch);                  // chunk stored at LDS slot lch
-                if (m0 + row < M && kbase + gch * 8 < K)
-                    __builtin_amdgcn_global_load_lds(a + (int64_t)(m0 + row) * lda + kbase + gch * 8,
-                                                     sa + inst * 512, 16, 0, 0);
-            }
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // LDS offsets (elements, from a stage's base) of this lane's operand reads
+    int offw[KS][TN], offa[KS][TM];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+            const int row = wn * T::kWCols + 16 * i + col;
+            offw[ks][i] = T::kStageA + row * BK + T::slot(row, 4 * ks + grp) * 8;
         }
 #pragma unroll
-        for (int i = 0; i < kWPer; ++i) {
-            const int inst = wave + kWaves * i;
-            if (n0 + inst * kRowsPerInst < N) {
-                const int row = inst * kRowsPerInst + lrow;
-                const int gch = swz(row, lch);
-                if (n0 + row < N && kbase + gch * 8 < K)
-                    __builtin_amdgcn_global_load_lds(wt + (int64_t)(n0 + row) * ldw + kbase + gch * 8,
-                                                     sw + inst * 512, 16, 0, 0);
+        for (int j = 0; j < TM; ++j) {
+            const int row = wm * T::kWRows + 16 * j + col;
+            offa[ks][j] = row * BK + T::slot(row, 4 * ks + grp) * 8;
+        }
+    }
+    // operands of one k tile, all 32-wide chunks, from LDS slot s
+    typedef bf16x8 OpW[KS][TN];
+    typedef bf16x8 OpA[KS][TM];
+    // (kGuard: skip k chunks past K and 16-row groups entirely past M)
+    auto read_ops = [&](auto guard, int s, int nks, OpW& fw, OpA& fa) __attribute__((always_inline)) {
+        constexpr bool kGuard = decltype(guard)::value;
+        const uint16_t* st = smem + s * T::kStage;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (!kGuard || ks < nks) {
+#pragma unroll
+                for (int i = 0; i < TN; ++i) fw[ks][i] = *reinterpret_cast<const bf16x8*>(st + offw[ks][i]);
+#pragma unroll
+                for (int j = 0; j < TM; ++j)
+                    if (!kGuard || j < tmv) fa[ks][j] = *reinterpret_cast<const bf16x8*>(st + offa[ks][j]);
             }
         }
     };
+    // the chain steps of one k tile: chunks ascending
+    auto mma = [&](auto guard, int nks, const OpW& fw, const OpA& fa) __attribute__((always_inline)) {
+        constexpr bool kGuard = decltype(guard)::value;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            if (!kGuard || ks < nks)
+#pragma unroll
+                for (int j = 0; j < TM; ++j)
+                    if (!kGuard || j < tmv)
+#pragma unroll
+                        for (int i = 0; i < TN; ++i) acc[i][j] = mfma16(fw[ks][i], fa[ks][j], acc[i][j]);
+    };
+    constexpr std::false_type kFull{};
+    constexpr std::true_type kEdge{};
 
-    // loads this wave issues per stage (wave-uniform, the same for every stage)
-    int per_stage = 0;
+    // Pipeline (both paths): S LDS stages.  At step kt the MFMAs of k tile kt
+    // run on operands read from LDS during step kt-1 while the operands of
+    // k tile kt+1 are read, and stage kt+S is loaded into the slot stage kt
+    // left once every wavefront has read it (its LDS reads done + barrier).
+    OpW fw0, fw1;
+    OpA fa0, fa1;
+    if (m0 + BM <= M && n0 + BN <= N && K % BK == 0) {
+        // ---- tile wholly inside M, N and a whole number of k tiles: no guards
+        // per-lane element offsets from the tile's first row (fixed for the
+        // whole k loop; k moves the wave-uniform base)
+        uint32_t ga[T::kAPer], gw[T::kWPer];
 #pragma unroll
-    for (int i = 0; i < kAPer; ++i) per_stage += (m0 + (wave + kWaves * i) * kRowsPerInst < M);
-#pragma unroll
-    for (int i = 0; i < kWPer; ++i) per_stage += (n0 + (wave + kWaves * i) * kRowsPerInst < N);
-
-    // 16-row groups of this wave that hold at least one row < M
-    const int wrow0 = m0 + wm * (kBM / kWM);
-    const int tmv = max(0, min(kTM, (M - wrow0 + 15) / 16));
-
-    f32x4 acc[kTN][kTM];
-    f32x4 acc2[kTN][kTM];          // second chain, used only by kOrder == 1
-#pragma unroll
-    for (int i = 0; i < kTN; ++i)
-#pragma unroll
-        for (int j = 0; j < kTM; ++j) {
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc2[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < T::kAPer; ++i) {
+            const int row = (wave + T::kWaves * i) * T::kRowsPerLoad + lrow;
+            ga[i] = (uint32_t)(row * lda + T::slot(row, lch) * 8);
         }
-
 #pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-        if (s < KT) issue(s, s);
-
-    for (int kt = 0; kt < KT; ++kt) {
-        // this wave's loads of stage kt have landed (later stages may still fly);
-        // then every wave's have, after the barrier
-        const int ahead = min(KT - 1 - kt, kStages - 2);
-        wait_vm_upto(ahead * per_stage);
-        asm volatile("s_barrier" ::: "memory");
-        if (kt + kStages - 1 < KT) issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
-
-        const uint16_t* sa = smem + (kt % kStages) * (kStageA + kStageW);
-        const uint16_t* sw = sa + kStageA;
-        const int nks = min(kBK, K - kt * kBK) / 32;       // 32-wide k chunks in this tile
-        // operands of one 32-wide k chunk, read from LDS
-        auto read_ops = [&](int ks, bf16x8 (&fw)[kTN], bf16x8 (&fa)[kTM]) __attribute__((always_inline)) {
+        for (int i = 0; i < T::kWPer; ++i) {
+            const int row = (wave + T::kWaves * i) * T::kRowsPerLoad + lrow;
+            gw[i] = (uint32_t)(row * ldw + T::slot(row, lch) * 8);
+        }
+        const uint16_t* a_tile = a + (int64_t)m0 * lda;
+        const uint16_t* w_tile = wt + (int64_t)n0 * ldw;
+        auto issue = [&](int kt, int s) __attribute__((always_inline)) {
+            uint16_t* sa = smem + s * T::kStage;
+            uint16_t* sw = sa + T::kStageA;
+            const uint16_t* ak = a_tile + kt * BK;
+            const uint16_t* wk = w_tile + kt * BK;
 #pragma unroll
-            for (int i = 0; i < kTN; ++i) {
-                const int row = wn * (kBN / kWN) + 16 * i + col;
-                fw[i] = *reinterpret_cast<const bf16x8*>(sw + row * kBK + swz(row, 4 * ks + grp) * 8);
-            }
+            for (int i = 0; i < T::kAPer; ++i)
+                gemm_load_lds16(ak + ga[i], sa + (wave + T::kWaves * i) * 512);
 #pragma unroll
-            for (int j = 0; j < kTM; ++j) {
-                const int row = wm * (kBM / kWM) + 16 * j + col;
-                fa[j] = *reinterpret_cast<const bf16x8*>(sa + row * kBK + swz(row, 4 * ks + grp) * 8);
-            }
+            for (int i = 0; i < T::kWPer; ++i)
+                gemm_load_lds16(wk + gw[i], sw + (wave + T::kWaves * i) * 512);
         };
-        // the chain step of one k chunk (ascending ks within the tile)
-        auto chain = [&](int ks, const bf16x8 (&fw)[kTN], const bf16x8 (&fa)[kTM]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int j = 0; j < kTM; ++j) {
-                if (j < tmv) {
+        for (int s = 0; s < S; ++s)
+            if (s < KT) issue(s, s);
+        if (KT >= S) gemm_wait_vm<(S - 1) * T::kPer>();
+        else gemm_wait_vm<0>();
+        gemm_barrier();
+        read_ops(kFull, 0, KS, fw0, fa0);
+        // steady state: the same unconditional wait every step
+        auto step = [&](int kt, const OpW& fwc, const OpA& fac, OpW& fwn, OpA& fan) __attribute__((always_inline)) {
+            gemm_wait_vm<(S - 2) * T::kPer>();       // stage kt+1 landed (own loads), own reads of kt done
+            gemm_barrier();                          // ... for every wavefront
+            issue(kt + S, kt % S);
+            read_ops(kFull, (kt + 1) % S, KS, fwn, fan);
+            mma(kFull, KS, fwc, fac);
+        };
+        // the last S k tiles: nothing left to load
+        auto step_tail = [&](int kt, const OpW& fwc, const OpA& fac, OpW& fwn, OpA& fan) __attribute__((always_inline)) {
+            gemm_wait_vm<0>();
+            gemm_barrier();
+            if (kt + 1 < KT) read_ops(kFull, (kt + 1) % S, KS, fwn, fan);
+            mma(kFull, KS, fwc, fac);
+        };
+        int kt = 0;
+        for (; kt + 1 + S < KT; kt += 2) {
+            step(kt, fw0, fa0, fw1, fa1);
+            step(kt + 1, fw1, fa1, fw0, fa0);
+        }
+        if (kt + S < KT) {
+            step(kt, fw0, fa0, fw1, fa1);
+            ++kt;
+            for (; kt + 1 < KT; kt += 2) {
+                step_tail(kt, fw1, fa1, fw0, fa0);
+                step_tail(kt + 1, fw0, fa0, fw1, fa1);
+            }
+            if (kt < KT) step_tail(kt, fw1, fa1, fw0, fa0);
+        } else {
+            for (; kt + 1 < KT; kt += 2) {
+                step_tail(kt, fw0, fa0, fw1, fa1);
+                step_tail(kt + 1, fw1, fa1, fw0, fa0);
+            }
+            if (kt < KT) step_tail(kt, fw0, fa0, fw1, fa1);
+        }
+    } else {
+        // ---- edge tile (rows past M, columns past N, a K tail): rows out of
+        // range are neither loaded nor stored; the load count per stage then
+        // depends on how many rows are in range (wave-uniform)
+        auto issue = [&](int kt, int s) __attribute__((always_inline)) {
+            uint16_t* sa = smem + s * T::kStage;
+            uint16_t* sw = sa + T::kStageA;
+            const int kbase = kt * BK;
 #pragma unroll
-                    for (int i = 0; i < kTN; ++i) {
-                        if (kOrder == 1 && (ks & 1))
-                            acc2[i][j] = mfma16(fw[i], fa[j], acc2[i][j]);
-                        else
-                            acc[i][j] = mfma16(fw[i], fa[j], acc[i][j]);
-                    }
+            for (int i = 0; i < T::kAPer; ++i) {
+                const int inst = wave + T::kWaves * i;
+                if (m0 + inst * T::kRowsPerLoad < M) {             // wave-uniform
+                    const int row = inst * T::kRowsPerLoad + lrow;
+                    const int gch = T::slot(row, lch);              // chunk landing at slot lch
+                    if (m0 + row < M && kbase + gch * 8 < K)
+                        gemm_load_lds16(a + (int64_t)(m0 + row) * lda + kbase + gch * 8, sa + inst * 512);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < T::kWPer; ++i) {
+                const int inst = wave + T::kWaves * i;
+                if (n0 + inst * T::kRowsPerLoad < N) {
+                    const int row = inst * T::kRowsPerLoad + lrow;
+                    const int gch = T::slot(row, lch);
+                    if (n0 + row < N && kbase + gch * 8 < K)
+                        gemm_load_lds16(wt + (int64_t)(n0 + row) * ldw + kbase + gch * 8, sw + inst * 512);
                 }
             }
         };
-        if (tmv > 0) {                                     // wave-uniform: rows < M in this wave's tile
-            if (nks == kBK / 32) {
-                // whole tile: every operand read is issued before the first MFMA,
-                // so the LDS latency is paid once per tile, not once per k chunk
-                bf16x8 fw[kBK / 32][kTN], fa[kBK / 32][kTM];
+        // loads this wavefront issues per stage (wave-uniform, the same for every stage;
+        // a load whose first row is in range has at least one active lane)
+        int per_stage = 0;
 #pragma unroll
-                for (int ks = 0; ks < kBK / 32; ++ks) read_ops(ks, fw[ks], fa[ks]);
-                __builtin_amdgcn_sched_barrier(0);                 // keep the reads ahead
+        for (int i = 0; i < T::kAPer; ++i) per_stage += (m0 + (wave + T::kWaves * i) * T::kRowsPerLoad < M);
 #pragma unroll
-                for (int ks = 0; ks < kBK / 32; ++ks) chain(ks, fw[ks], fa[ks]);
-            } else {
-                for (int ks = 0; ks < nks; ++ks) {               // K tail
-                    bf16x8 fw[kTN], fa[kTM];
-                    read_ops(ks, fw, fa);
-                    chain(ks, fw, fa);
-                }
+        for (int i = 0; i < T::kWPer; ++i) per_stage += (n0 + (wave + T::kWaves * i) * T::kRowsPerLoad < N);
+        auto nks_of = [&](int kt) { return min(BK, K - kt * BK) / 32; };
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+            if (s < KT) issue(s, s);
+        gemm_wait_vm_upto(min(KT - 1, S - 1) * per_stage);
+        gemm_barrier();
+        if (tmv > 0) read_ops(kEdge, 0, nks_of(0), fw0, fa0);
+        auto step = [&](int kt, const OpW& fwc, const OpA& fac, OpW& fwn, OpA& fan) __attribute__((always_inline)) {
+            gemm_wait_lds();                                                    // own reads of stage kt done
+            gemm_wait_vm_upto(max(0, min(KT - 2 - kt, S - 2)) * per_stage);     // stage kt+1 landed
+            gemm_barrier();
+            if (kt + S < KT) issue(kt + S, kt % S);
+            if (tmv > 0) {
+                if (kt + 1 < KT) read_ops(kEdge, (kt + 1) % S, nks_of(kt + 1), fwn, fan);
+                mma(kEdge, nks_of(kt), fwc, fac);
             }
+        };
+        int kt = 0;
+        for (; kt + 1 < KT; kt += 2) {
+            step(kt, fw0, fa0, fw1, fa1);
+            step(kt + 1, fw1, fa1, fw0, fa0);
         }
-        // the next iteration's barrier orders these LDS reads before any wave
-        // overwrites this slot
+        if (kt < KT) step(kt, fw0, fa0, fw1, fa1);
     }
 
-    // lane holds c[m = .. + col][n = .. + 4 grp + r], r = 0..3
+    // ---- epilogue: lane holds c[m = wrow0 + 16 j + col][n = .. + 4 grp + r], r = 0..3
 #pragma unroll
-    for (int i = 0; i < kTN; ++i) {
+    for (int i = 0; i < TN; ++i) {
 #pragma unroll
-        for (int j = 0; j < kTM; ++j) {
+        for (int j = 0; j < TM; ++j) {
             const int m = wrow0 + 16 * j + col;
-            const int n = n0 + wn * (kBN / kWN) + 16 * i + 4 * grp;
+            const int n = n0 + wn * T::kWCols + 16 * i + 4 * grp;
             if (m < M && n < N) {
                 f32x4 v = acc[i][j];
-                if (kOrder == 1) v = v + acc2[i][j];
                 if (bias) {                               // addmm: the bias row, after the whole chain
                     const u32x2 bb = *reinterpret_cast<const u32x2*>(bias + n);
                     v[0] = v[0] + bf16_to_f32(bb[0] & 0xffffu);
@@ -252,24 +382,27 @@ static inline int gemm_validate(const void* a, int64_t lda, const void* wt, int6
                   !bi_aligned(c, c_dtype == BI_F32 ? 16 : 8)))
         return BI_ERR_INVALID_ARGUMENT;
     if ((K % 32) || (N % 4)) return BI_ERR_UNSUPPORTED;
-    if (M > 0x7fffffffLL - kBM || N > 0x7fffffffLL - kBN || K > 0x7fffffffLL - kBK)
+    // per-lane load offsets inside a tile are 32-bit: rows of up to 2^24 elements
+    if (lda >= (1LL << 24) || ldw >= (1LL << 24)) return BI_ERR_UNSUPPORTED;
+    if (M > 0x7fffffffLL - BiTile::kBM || N > 0x7fffffffLL - BiTile::kBN || K > 0x7fffffffLL - BiTile::kBK)
         return BI_ERR_UNSUPPORTED;
-    const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    // the baseline's tiles are no smaller than 64 x 32
+    const int64_t tiles = ((M + 63) / 64) * ((N + 31) / 32);
     if (tiles > 0x7fffffffLL - 8) return BI_ERR_UNSUPPORTED;
     if (M == 0) return -1;
     return BI_OK;
 }
 
-template <int kOrder>
+template <class T, bool kSplitK = false>
 static inline int gemm_launch(const void* a, int64_t lda, const void* wt, int64_t ldw, const void* bias,
                               void* c, int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K,
-                              void* stream)
+                              void* stream, int splits = 1, int64_t c_split_stride = 0)
 {
-    const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    const int64_t tiles = ((M + T::kBM - 1) / T::kBM) * ((N + T::kBN - 1) / T::kBN);
     const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
-    hipLaunchKernelGGL(gemm_kernel<kOrder>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL((gemm_kernel<T, kSplitK>), dim3(grid, splits), dim3(T::kThreads), 0, (hipStream_t)stream,
                        (const uint16_t*)a, lda, (const uint16_t*)wt, ldw, (const uint16_t*)bias, c, ldc,
-                       c_dtype == BI_F32 ? 1 : 0, (int)M, (int)N, (int)K);
+                       c_dtype == BI_F32 ? 1 : 0, (int)M, (int)N, (int)K, c_split_stride);
     return bi_launch_status();
 }
 
