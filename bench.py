@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip", default="", help="comma list of phases to skip: decode,prefill")
+    ap.add_argument("--no-toy", action="store_true",
+                    help="skip the toy-decoder experiment through both libraries")
+    ap.add_argument("--toy-runs", type=int, default=100)
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the supplementary points (RMSNorm 1 GiB, log_softmax, decode S sweep, prefill P sweep)")
     return ap.parse_args()
@@ -215,27 +218,14 @@ def main():
 
     # ------------------------------------------------------------ one step
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    rec = {"gemm": [], "rms": [], "phase1": [], "decode": [], "prefill": []}
+    rec = {"phase1": [], "decode": [], "prefill": []}
     rot = WeightRotation()
 
-    def phase1(record: bool):
+    def phase1(record: bool = False):
         for M in I.M_SWEEP:
-            if record:
-                rs, re_ = E(), E()
-                rs.record(stream)
             ops.bi_rmsnorm(x[:M], wn, I.LLAMA_EPS, y=y[:M], want_rstd=False)
-            if record:
-                re_.record(stream)
-                rec["rms"].append((rs, re_, M))
             for N in Ns:
-                wt = W[N][rot.next(N)]
-                if record:
-                    gs, ge = E(), E()
-                    gs.record(stream)
-                ops.bi_matmul(y[:M], wt, c=C[N][:M])
-                if record:
-                    ge.record(stream)
-                    rec["gemm"].append((gs, ge, 2 * M * N * H, M, N))
+                ops.bi_matmul(y[:M], W[N][rot.next(N)], c=C[N][:M])
 
     def phase2():
         ops.bi_kv_append(knew, vnew, slots, kc, vc)
@@ -265,6 +255,9 @@ def main():
         graphs[name] = gph
     torch.cuda.synchronize()
 
+    def total_ms(pairs):
+        return sum(a.elapsed_time(b) for a, b, *_ in pairs)
+
     def step(record: bool):
         for name, _ in phases:
             if record:
@@ -289,39 +282,64 @@ def main():
     sclk_after = gpu_sclk_mhz()
     # the replayed sweep ends with M=2048: its first rows must equal the eager run bit for bit
     graph_matches_eager = bool(torch.equal(C[14336][:64].view(torch.int16), ref_c.view(torch.int16)))
-    # per-launch durations of bi_matmul: eager passes of the same sweep, a HIP
-    # event pair around every launch.  Each pass is queued behind a few graph
-    # replays of the sweep, so the host has queued every launch before the GPU
-    # reaches it and an event pair brackets the kernel, not host launch gaps.
-    head = 3
-    host_enqueue_ms = []
-    for _ in range(max(2, args.steps // 2)):
-        for _ in range(head):
-            graphs["phase1"].replay()
-        th = time.perf_counter()
-        phase1(True)
-        host_enqueue_ms.append((time.perf_counter() - th) * 1e3)
-    torch.cuda.synchronize()
+    # Per-launch durations without host launch gaps: the sweep's 138 GEMM
+    # launches captured as one HIP graph (the RMSNorms left out), each shape as
+    # a graph of 4 launches over its 4 weight copies, and the 69 RMSNorms as one
+    # graph; HIP events on the stream the graphs are replayed on bracket the
+    # replays (median of several).
+    def capture(fn):
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            fn()
+        return gph
 
-    def total_ms(pairs):
-        return sum(a.elapsed_time(b) for a, b, *_ in pairs)
+    def replay_ms(gph, reps):
+        gph.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a_, b_ = E(), E()
+            a_.record(stream)
+            gph.replay()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a_.elapsed_time(b_))
+        return float(np.median(ts))
 
+    def gemm_sweep_only():
+        for M in I.M_SWEEP:
+            for N in Ns:
+                ops.bi_matmul(y[:M], W[N][rot.next(N)], c=C[N][:M])
+
+    def rms_sweep_only():
+        for M in I.M_SWEEP:
+            ops.bi_rmsnorm(x[:M], wn, I.LLAMA_EPS, y=y[:M], want_rstd=False)
+
+    reps = max(5, args.steps)
+    g_gemm = capture(gemm_sweep_only)
+    gemm_ms = replay_ms(g_gemm, reps)                     # one sweep of 138 launches
+    del g_gemm
+    g_rms = capture(rms_sweep_only)
+    rms_ms = replay_ms(g_rms, reps)
+    del g_rms
+    order = [(M, N) for M in I.M_SWEEP for N in Ns]
+    n_launch = len(order)
+    gemm_flops = sum(2 * M * N * H for (M, N) in order)
+    gemm_bytes = sum(2 * (M * H + N * H + M * N) for (M, N) in order)
+    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    traffic = traffic_from_profile()
     phase1_ms = total_ms(rec["phase1"]) / args.steps
     value = gemm_flops_step / (phase1_ms * 1e-3) / 1e12
-    gemm_ms = total_ms(rec["gemm"])
-    gemm_flops = sum(r[2] for r in rec["gemm"])
-    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
-    n_launch = len(rec["gemm"])
-    traffic = traffic_from_profile()
-    gemm_bytes = sum(2 * (M * H + N * H + M * N) for (_, _, _, M, N) in rec["gemm"])
 
-    # per-M table (median over steps)
-    per = {}
-    for (a, b, fl, M, N) in rec["gemm"]:
-        per.setdefault((M, N), []).append(a.elapsed_time(b))
+    # per-shape table: a graph of 4 launches of the shape, one per weight copy
+    per_us = {}
+    for (M, N) in order:
+        gph = capture(lambda: [ops.bi_matmul(y[:M], W[N][rot.next(N)], c=C[N][:M]) for _ in range(N_WEIGHT_COPIES)])
+        per_us[(M, N)] = replay_ms(gph, 3) * 1e3 / N_WEIGHT_COPIES
+        del gph
     sweep = []
-    for (M, N), ts in sorted(per.items()):
-        t = float(np.median(ts)) * 1e-3
+    for (M, N) in sorted(per_us):
+        t = per_us[(M, N)] * 1e-6
         fl = 2 * M * N * H
         byt = 2 * (M * H + N * H + M * N)
         roof_t = max(fl / (PEAK_BF16_TFLOPS * 1e12), byt / (PEAK_HBM_GBS * 1e9))
@@ -336,10 +354,9 @@ def main():
     else:
         bound, achieved_r, peak_r, unit_r = "mfma", achieved, PEAK_BF16_TFLOPS, "TFLOP/s"
     roof_total = sum(max(2 * M * N * H / (PEAK_BF16_TFLOPS * 1e12), 2 * (M * H + N * H + M * N) / (PEAK_HBM_GBS * 1e9))
-                     for (M, N) in per)
-    meas_total = sum(float(np.median(ts)) * 1e-3 for ts in per.values())
-    rms_ms = total_ms(rec["rms"])
-    rms_bytes = sum(4 * M * H + 2 * H for (_, _, M) in rec["rms"])
+                     for (M, N) in order)
+    meas_total = sum(per_us.values()) * 1e-6
+    rms_bytes = sum(4 * M * H + 2 * H for M in I.M_SWEEP)
 
     result = {
         "metric": METRIC,
@@ -378,15 +395,17 @@ def main():
             "flops_per_launch_avg": gemm_flops / n_launch,
             "algorithmic_bytes_per_launch_avg": gemm_bytes / n_launch,
             "frac_of_min_roofline": round(roof_total / meas_total, 4),
-            "timing": (f"event pair per launch in eager sweeps queued behind {head} graph replays "
-                       f"({head * phase1_ms:.1f} ms of GPU work); host queued each sweep in "
-                       f"{max(host_enqueue_ms):.1f} ms at most"),
+            "timing": ("the sweep's 138 GEMM launches as one HIP graph (no RMSNorm), replayed "
+                       f"{reps} times, median; HIP events on the replaying stream"),
             "source_hash": src_hash(*GEMM_SOURCES),
         },
         "gemm_sweep": sweep,
+        "gemm_sweep_timing": "each shape as a HIP graph of 4 launches, one per weight copy (N=4096: the 4 copies, "
+                             "134 MB, can stay in the 256 MB last-level cache; N=14336: 470 MB cannot)",
         "rmsnorm": {"GB/s": round(rms_bytes / (rms_ms * 1e-3) / 1e9, 1),
                     "frac_hbm": round(rms_bytes / (rms_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                    "note": "M=1..2048 rows of 4096, launch-latency bound at this size"},
+                    "note": "the 69 RMSNorms of the sweep (M=1..2048 rows of 4096) as one HIP graph; "
+                            "launch-latency bound at this size"},
     }
     if "decode" not in skip:
         dms = total_ms(rec["decode"]) / args.steps
@@ -553,6 +572,58 @@ def main():
     except Exception as e:  # context only
         result["baseline_hipblaslt"] = {"error": str(e)[:200]}
 
+    # ------------------------------------------------------------ toy decoder, both libraries
+    # The pages' end-to-end experiment (one prompt decoded greedily many times
+    # under a varying co-batched load) through the invariant library and the
+    # shape-tuned non-invariant one, on the same load schedule (the schedule is
+    # drawn from its own seed, not from the tokens): wall time, tokens/s and
+    # the number of distinct completions of each.
+    toy_w = None
+    if not args.no_toy:
+        try:
+            from invariant_bi_rmsnorm_amd.toy import Request, ToyEngine, run_load_experiment
+            log("toy: weights")
+            toy_w = I.toy_weights(I.TOY)
+            prompt = I.toy_prompt(I.TOY, 64)
+            n_new = 256
+            eng = {"invariant": ToyEngine(I.TOY, toy_w, 4096, 1024, 64, 1024)}
+            prev = ops.use_library(ops.NB_LIB_PATH)
+            try:
+                eng["nb"] = ToyEngine.sharing(eng["invariant"])
+            finally:
+                ops.use_library(prev)
+            toy = {"runs": args.toy_runs, "tokens_per_run": n_new, "prompt": 64, "load_seed": 5002,
+                   "schedule": "continuous batching of 0-63 other requests (1-512-token prompts, 1-256 new "
+                               "tokens), prefill chunks of 16-512 tokens, batch order shuffled every step"}
+            for name in ("invariant", "nb"):
+                e = eng[name]
+                # first step alone on the GPU: the 64-token prompt, as the oracle times it below
+                r = Request(10 ** 9, prompt, 1, target=True)
+                torch.cuda.synchronize()
+                t0s = time.perf_counter()
+                e.step([(r, len(prompt))])
+                torch.cuda.synchronize()
+                first_s = time.perf_counter() - t0s
+                e.release(r)
+                log(f"toy: {args.toy_runs} runs x {n_new} tokens through {name}")
+                e.tokens_processed = 0
+                torch.cuda.synchronize()
+                t0s = time.perf_counter()
+                hashes, stats = run_load_experiment(e, prompt, args.toy_runs, n_new, seed=5002)
+                torch.cuda.synchronize()
+                dt = time.perf_counter() - t0s
+                toy[name] = {"s": round(dt, 3), "unique_completions": len(set(hashes)),
+                             "target_tokens_per_s": round(args.toy_runs * n_new / dt, 1),
+                             "engine_tokens_per_s": round(e.tokens_processed / dt, 1),
+                             "engine_tokens": e.tokens_processed, "steps": stats["steps"],
+                             "co_load_mean": round(stats["co_load_mean"], 1),
+                             "first_step_prompt64_s": round(first_s, 5)}
+            toy["invariant_over_nb_time"] = round(toy["invariant"]["s"] / toy["nb"]["s"], 3)
+            result["toy_experiment"] = toy
+            del eng
+        except Exception as e:  # context only: never lose the result line for it
+            result["toy_experiment"] = {"error": f"{type(e).__name__}: {e}"[:300]}
+
     # ------------------------------------------------------------ CPU oracle baseline
     if not args.no_cpu_baseline:
         import oracle
@@ -570,10 +641,43 @@ def main():
             if time.perf_counter() - t > 3 * args.cpu_seconds:
                 break
         dt = time.perf_counter() - t
+        cores = oracle.num_threads()
         result["cpu_baseline"] = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
-                                  "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
+                                  "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
                                   "sample": f"oracle matmul (fp64) of {done} of the sweep's {2 * len(I.M_SWEEP)} "
                                             f"GEMMs ({fl / 1e9:.0f} GFLOP of {gemm_flops_step / 1e9:.0f}), {dt:.1f} s"}
+        # the same oracle on one thread, on the sweep's first GEMMs (bounded)
+        try:
+            oracle.set_num_threads(1)
+            fl1, done1, t = 0, 0, time.perf_counter()
+            for M in I.M_SWEEP:
+                for N in Ns:
+                    oracle.matmul(a[:M], wts[N])
+                    fl1 += 2 * M * N * H
+                    done1 += 1
+                if time.perf_counter() - t > args.cpu_seconds / 2:
+                    break
+            dt1 = time.perf_counter() - t
+            result["cpu_baseline"]["single_thread"] = {
+                "value": round(fl1 / dt1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                "sample": f"the sweep's first {done1} GEMMs ({fl1 / 1e9:.1f} GFLOP), {dt1:.1f} s"}
+        except Exception as e:  # context only
+            result["cpu_baseline"]["single_thread"] = {"error": f"{type(e).__name__}: {e}"[:200]}
+        finally:
+            oracle.set_num_threads(cores)
+        # the toy decoder's first step (64-token prompt -> logits of its last token)
+        if toy_w is not None:
+            try:
+                t = time.perf_counter()
+                oracle.toy_forward(I.TOY, toy_w, I.toy_prompt(I.TOY, 64))
+                dtt = time.perf_counter() - t
+                gpu_first = result.get("toy_experiment", {}).get("invariant", {}).get("first_step_prompt64_s")
+                result["cpu_baseline"]["toy_first_step"] = {
+                    "cpu_s": round(dtt, 3), "cores": cores, "gpu_s": gpu_first,
+                    "note": "oracle toy_forward over the 64-token prompt (fp64, 8 layers, vocab 32000) vs the "
+                            "invariant engine's step on the same prompt (host-timed, includes one host sync)"}
+            except Exception as e:  # context only
+                result["cpu_baseline"]["toy_first_step"] = {"error": f"{type(e).__name__}: {e}"[:200]}
 
         # the oracle beside the other rows, on bounded samples of the same work
         # (GPU times from this run: the instrumented sweep and the supplementary points)
@@ -585,9 +689,11 @@ def main():
                 fn()
                 return time.perf_counter() - t0
 
-            rms_2048 = [a.elapsed_time(b) * 1e3 for (a, b, M) in rec["rms"] if M == 2048]
+            g2048 = capture(lambda: ops.bi_rmsnorm(x[:2048], wn, I.LLAMA_EPS, y=y[:2048], want_rstd=False))
+            rms_2048_us = replay_ms(g2048, 5) * 1e3
+            del g2048
             dt = timed(lambda: oracle.rmsnorm(I.llama_x(2048), I.llama_norm_weight(), I.LLAMA_EPS))
-            beside["rmsnorm_2048x4096"] = {"cpu_s": round(dt, 3), "gpu_us": round(float(np.median(rms_2048)), 2)}
+            beside["rmsnorm_2048x4096"] = {"cpu_s": round(dt, 3), "gpu_us": round(rms_2048_us, 2)}
             sup = result.get("supplementary", {})
             if "log_softmax_256x32000" in sup:
                 xl = (np.random.default_rng(7).standard_normal((256, 32000)) * 3).astype(np.float32)

@@ -9,7 +9,8 @@
 //   * M <= 64: split-K.  The 64 x 32 x 128 tile (enough workgroups to stream
 //     the weights) computes z = 0..Z-1 partial products over k slices of
 //     K / Z into fp32 scratch, Z chosen so that about 512 workgroups run; a
-//     second kernel adds the partials in z order and rounds.  Each output's
+//     second kernel adds the partials in z order and rounds.  Where N alone
+//     gives that many workgroups (no split), the 128 x 64 tile runs instead.  Each output's
 //     sum is therefore split into Z pieces whose count depends on N and K --
 //     and the rows of a batch of 64 are summed differently from the same
 //     rows in a batch of 65.
@@ -24,8 +25,9 @@
 
 namespace {
 
-using NbSmallTile = GemmTile<64, 32, 128, 4, 2, 3>;
-using NbLargeTile = GemmTile<128, 128, 64, 2, 4, 3>;
+using NbSmallTile = GemmTile<64, 32, 128, 4, 2, 3, 1>;
+using NbMidTile = GemmTile<128, 64, 128, 4, 2, 3, 1>;       // the invariant library's tile
+using NbLargeTile = GemmTile<128, 128, 64, 2, 4, 3, 1>;
 
 constexpr size_t kNbScratchFloats = (size_t)16 << 20;     // 64 MiB of fp32 partials
 static __device__ __align__(256) float nb_scratch[kNbScratchFloats];
@@ -95,12 +97,13 @@ static int nb_gemm(const void* a, int64_t lda, const void* wt, int64_t ldw, cons
                                (const uint16_t*)bias, c, ldc, c_dtype == BI_F32 ? 1 : 0, (int)M, (int)N);
             return bi_launch_status();
         }
-        return gemm_launch<NbSmallTile>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+        // enough workgroups without a split (wide N): the 128 x 64 tile streams faster
+        return gemm_launch<NbMidTile>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     }
     const int64_t large_tiles = ((M + 127) / 128) * ((N + 127) / 128);
     if (large_tiles >= 512)
         return gemm_launch<NbLargeTile>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    return gemm_launch<BiTile>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    return gemm_launch<NbMidTile>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
 }
 
 }  // namespace

@@ -58,7 +58,9 @@ __device__ __forceinline__ void gemm_load_lds16(const uint16_t* g, uint16_t* l)
     __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+// kLib tags which library instantiates the tile (0: libbi.so, 1: the baseline),
+// so profiles tell their kernels apart; it has no other effect.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int kLib = 0>
 struct GemmTile {
     static constexpr int kBM = BM, kBN = BN, kBK = BK, kWM = WM, kWN = WN, kStages = STAGES;
     static constexpr int kWaves = WM * WN;
@@ -236,48 +238,28 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
             for (int i = 0; i < T::kWPer; ++i)
                 gemm_load_lds16(wk + gw[i], sw + (wave + T::kWaves * i) * 512);
         };
+        // Every step issues one stage: past the last k tile it loads the last k
+        // tile again into the slot just freed (never read again), so every
+        // wait below counts the same loads and one loop covers all k tiles.
 #pragma unroll
-        for (int s = 0; s < S; ++s)
-            if (s < KT) issue(s, s);
-        if (KT >= S) gemm_wait_vm<(S - 1) * T::kPer>();
-        else gemm_wait_vm<0>();
+        for (int s = 0; s < S; ++s) issue(min(s, KT - 1), s);
+        gemm_wait_vm<(S - 1) * T::kPer>();           // stage 0 landed (own loads)
         gemm_barrier();
         read_ops(kFull, 0, KS, fw0, fa0);
-        // steady state: the same unconditional wait every step
         auto step = [&](int kt, const OpW& fwc, const OpA& fac, OpW& fwn, OpA& fan) __attribute__((always_inline)) {
             gemm_wait_vm<(S - 2) * T::kPer>();       // stage kt+1 landed (own loads), own reads of kt done
             gemm_barrier();                          // ... for every wavefront
-            issue(kt + S, kt % S);
-            read_ops(kFull, (kt + 1) % S, KS, fwn, fan);
-            mma(kFull, KS, fwc, fac);
-        };
-        // the last S k tiles: nothing left to load
-        auto step_tail = [&](int kt, const OpW& fwc, const OpA& fac, OpW& fwn, OpA& fan) __attribute__((always_inline)) {
-            gemm_wait_vm<0>();
-            gemm_barrier();
+            issue(min(kt + S, KT - 1), kt % S);
             if (kt + 1 < KT) read_ops(kFull, (kt + 1) % S, KS, fwn, fan);
             mma(kFull, KS, fwc, fac);
         };
         int kt = 0;
-        for (; kt + 1 + S < KT; kt += 2) {
+        for (; kt + 1 < KT; kt += 2) {
             step(kt, fw0, fa0, fw1, fa1);
             step(kt + 1, fw1, fa1, fw0, fa0);
         }
-        if (kt + S < KT) {
-            step(kt, fw0, fa0, fw1, fa1);
-            ++kt;
-            for (; kt + 1 < KT; kt += 2) {
-                step_tail(kt, fw1, fa1, fw0, fa0);
-                step_tail(kt + 1, fw0, fa0, fw1, fa1);
-            }
-            if (kt < KT) step_tail(kt, fw1, fa1, fw0, fa0);
-        } else {
-            for (; kt + 1 < KT; kt += 2) {
-                step_tail(kt, fw0, fa0, fw1, fa1);
-                step_tail(kt + 1, fw1, fa1, fw0, fa0);
-            }
-            if (kt < KT) step_tail(kt, fw0, fa0, fw1, fa1);
-        }
+        if (kt < KT) step(kt, fw0, fa0, fw1, fa1);
+        gemm_wait_vm<0>();                           // no load may still write this LDS at exit
     } else {
         // ---- edge tile (rows past M, columns past N, a K tail): rows out of
         // range are neither loaded nor stored; the load count per stage then

@@ -57,21 +57,35 @@ def _one(pattern, d):
 
 
 def short(name: str) -> str:
+    # the GEMM template: libbi.so's one tile vs the baseline library's tiles (tag 1)
+    if "gemm_kernel<" in name:
+        return "gemm_kernel" if "GemmTile<128, 64, 128, 4, 2, 3, 0>" in name else "gemm_kernel (baseline lib)"
     for k in KERNELS:
         if name.startswith(k) or f" {k}" in name or name.startswith(f"(anonymous namespace)::{k}"):
             return k
     return name if len(name) <= 60 else name[:57] + "..."
 
 
+def trace_durations(d):
+    """{kernel: [duration in microseconds per dispatch]} from the per-dispatch
+    kernel trace of a --kernel-trace run, kernels named by short()."""
+    out = defaultdict(list)
+    for r in csv.DictReader(open(_one("*kernel_trace.csv", d))):
+        out[short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return out
+
+
 def stats_md(d, out, cmd, title):
-    rows = list(csv.DictReader(open(_one("*kernel_stats.csv", d))))
+    dur = trace_durations(d)
+    total = sum(sum(v) for v in dur.values())
     lines = [f"# {title}", "", "Command (from the repository root, one MI355X):", "", "```", cmd, "```", "",
-             "rocprofv3 kernel statistics (durations in microseconds):", "",
+             "Kernel durations from rocprofv3's per-dispatch kernel trace (microseconds), per kernel "
+             "instantiation: `gemm_kernel` is libbi.so's one GEMM tile, `gemm_kernel (baseline lib)` the "
+             "non-invariant library's tiles.", "",
              "| kernel | calls | total us | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
-    for r in rows:
-        lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
-                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
-                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    for k, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {k} | {len(v)} | {sum(v):.1f} | {sum(v) / len(v):.2f} | {min(v):.2f} | "
+                     f"{max(v):.2f} | {100 * sum(v) / total:.2f} |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -90,13 +104,8 @@ def read_counters(d):
 
 
 def avg_durations_us(trace_dir):
-    """{kernel: average duration in microseconds} from a --kernel-trace --stats run"""
-    out = {}
-    for r in csv.DictReader(open(_one("*kernel_stats.csv", trace_dir))):
-        k = short(r["Name"])
-        if k in KERNELS:
-            out[k] = float(r["AverageNs"]) / 1e3
-    return out
+    """{kernel: average duration in microseconds} from a --kernel-trace run"""
+    return {k: sum(v) / len(v) for k, v in trace_durations(trace_dir).items() if k in KERNELS}
 
 
 def traffic(fetch_dir, write_dir, out_md, out_json, cmd_fetch, cmd_write, trace_dir=None):

@@ -120,6 +120,7 @@ class ToyEngine:
         self.sampled = torch.empty((max_seqs,), dtype=torch.int32, device=device)
         self.free = list(range(num_blocks))[::-1]
         self.num_blocks = num_blocks
+        self.tokens_processed = 0       # tokens fed through step(), all requests
 
     @classmethod
     def sharing(cls, other: "ToyEngine") -> "ToyEngine":
@@ -136,6 +137,7 @@ class ToyEngine:
         e.next_ids = torch.empty_like(other.next_ids)
         e.logits = torch.empty_like(other.logits)
         e.sampled = torch.empty_like(other.sampled)
+        e.tokens_processed = 0
         return e
 
     # ---------------------------------------------------------------- blocks
@@ -189,6 +191,7 @@ class ToyEngine:
             table[s, :len(bl)] = bl
             max_q = max(max_q, n)
         T = q_start[-1]
+        self.tokens_processed += T
         extra = {}                      # s -> positions (rows) of its tokens before the last
         for s in sorted(set(all_rows)):
             first, last = q_start[s], q_start[s + 1] - 1

@@ -85,6 +85,7 @@ def _load():
     lib.or_lm_head_f64.argtypes = [P, I64, P, D, P, I64, P, I64, I64, I64, I64]
     lib.or_sample.argtypes = [P, I64, I64, I64, ctypes.c_float, P, P, P, P]
     lib.or_num_threads.restype = ctypes.c_int
+    lib.or_set_num_threads.argtypes = [ctypes.c_int]
     lib.or_rope.argtypes = [P, P, P, I64, I32, I32, D]
     lib.or_silu_mul.argtypes = [P, P, P, I64]
     lib.or_add.argtypes = [P, P, P, I64]
@@ -108,6 +109,11 @@ def _u16(a) -> np.ndarray:
 
 def num_threads() -> int:
     return int(_load().or_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the row-parallel loops from now on (the results do not depend on it)."""
+    _load().or_set_num_threads(int(n))
 
 
 # --------------------------------------------------------------------------

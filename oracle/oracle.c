@@ -452,6 +452,16 @@ void or_lm_head_f64(const uint16_t* h, int64_t ldh, const uint16_t* w, double ep
     free(y);
 }
 
+/* thread count of the row-parallel loops (results do not depend on it) */
+void or_set_num_threads(int n)
+{
+#if defined(_OPENMP)
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int or_num_threads(void)
 {
 #if defined(_OPENMP)
