@@ -33,6 +33,19 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nvalid)
     return v;
 }
 
+// workgroup barrier for LDS hand-offs: this wave's LDS accesses done, then
+// s_barrier, without the memory fence of __syncthreads (which would also wait
+// for the value loads still in flight)
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// loads issued per lane per item for the values operands (all unconditional,
+// so the count is fixed: the wait for K below leaves exactly these in flight)
+constexpr int kVLoads = 2 * kChunks;
+
 // K rows of a split are staged in LDS (256 B per token row); 16-byte chunk ch
 // of row r sits at slot ch ^ kswz(r), so the 16 rows one MFMA operand read
 // touches fall in distinct banks.
@@ -42,7 +55,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t num_blocks, const int32_t* __restrict__ bt,
     int max_blocks, const int32_t* __restrict__ kv_lens, int S, int Hq, int Hkv,
-    int max_splits, int split_len, float scale_log2, float* __restrict__ ws)
+    int max_splits, int split_len, float scale_log2, float* __restrict__ ws, uint16_t* __restrict__ out,
+    int64_t ldo)
 {
     __shared__ int s_off[kMaxSeqs + 1];
     __shared__ int s_part[kThreads];
@@ -112,53 +126,44 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
             if (tok < L) blk = btr[tok >> 4];
             s_blk[tid] = (blk >= 0 && blk < num_blocks) ? blk : -1;
         }
-        __syncthreads();
+        lds_barrier();
 
         // tokens of a block whose id is outside the pool do not exist for the
         // arithmetic: score -inf, weight 0, value 0 (their K rows are never
         // loaded, so nothing stale from an earlier item can reach the result)
+        int blk16[kSplit / kBlock];                  // the 16 ids in registers (broadcast reads, once)
+#pragma unroll
+        for (int b = 0; b < kSplit / kBlock; ++b) blk16[b] = s_blk[b];
+        // block of this lane's tokens 32 c + 8 grp .. + 7 (blk16[2c] or blk16[2c+1]),
+        // chosen with bit operations so the array is never indexed per lane
+        const int hi_mask = -(grp >> 1);
+        auto lane_blk = [&](int c) __attribute__((always_inline)) {
+            return blk16[2 * c] ^ ((blk16[2 * c] ^ blk16[2 * c + 1]) & hi_mask);
+        };
         bool bad = false;
 #pragma unroll
-        for (int b = 0; b < kSplit / kBlock; ++b) bad |= (t0 + kBlock * b < L) && s_blk[b] < 0;
+        for (int b = 0; b < kSplit / kBlock; ++b) bad |= (t0 + kBlock * b < L) && blk16[b] < 0;
         // a split that ends before the sequence does and reads only valid
         // blocks needs no masking (the masked code gives the same values
         // there, with more instructions)
         const bool whole = t0 + kSplit <= L && !bad;
 
-        // values operands of this wave's two head-dim tiles, all 8 chunks
-        // (issued first: they do not depend on the scores)
-        u32x4 vv[kChunks][2];
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-            const int tok = t0 + 32 * c + 8 * grp;
-            const int blk = tok < L ? s_blk[(tok - t0) >> 4] : -1;
-            const bool ok = blk >= 0;
-#pragma unroll
-            for (int dd = 0; dd < 2; ++dd) {
-                const int d = 16 * (2 * wave + dd) + col;
-                vv[c][dd] = zero_u32x4();
-                if (ok) {
-                    vv[c][dd] = ld16(vc + (((int64_t)blk * Hkv + g) * kD + d) * kBlock + (tok & 15));
-                    if (!whole && tok + 8 > L) vv[c][dd] = keep_first(vv[c][dd], L - tok);
-                }
-            }
-        }
-
-        // query operands: column col is query head g*G + col
-        bf16x8 qf[4];
+        // query operands: column col is query head g*G + col (columns past the
+        // group read head g*G's row and are zeroed)
         const bool qok = col < G;
-        const uint16_t* qrow = q + (int64_t)s * ldq + (int64_t)(g * G + col) * kD + 8 * grp;
+        const uint16_t* qrow = q + (int64_t)s * ldq + (int64_t)(g * G + (qok ? col : 0)) * kD + 8 * grp;
+        u32x4 qraw[4];
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) qf[dc] = as_bf16x8(qok ? ld16(qrow + 32 * dc) : zero_u32x4());
+        for (int dc = 0; dc < 4; ++dc) qraw[dc] = ld16(qrow + 32 * dc);
 
         // K of the split -> LDS, one 1 KB wave load = 4 token rows of 256 B
         // (rows past the sequence are not loaded; their scores are masked)
 #pragma unroll
         for (int it = 0; it < kSplit / 4 / 4; ++it) {
             const int inst = wave + 4 * it;
-            const int row = 4 * inst + (lane >> 4);
+            const int row = 4 * inst + (lane >> 4);          // row >> 4 == it: the 4 rows lie in block it
             const int tok = t0 + row;
-            const int blk = tok < L ? s_blk[row >> 4] : -1;
+            const int blk = tok < L ? blk16[it] : -1;
             if (blk >= 0) {
                 const int gch = (lane & 15) ^ kswz(row);         // chunk landing at slot lane&15
                 __builtin_amdgcn_global_load_lds(
@@ -166,7 +171,29 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
                     s_k + inst * 512, 16, 0, 0);
             }
         }
-        __syncthreads();      // waits for this wave's loads, then for everyone's
+
+        // values operands of this wave's two head-dim tiles, all 8 chunks,
+        // issued last so that they land while the scores are formed; every
+        // lane loads (tokens without a block read block 0 and are zeroed at use)
+        u32x4 vv[kChunks][2];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int tok = t0 + 32 * c + 8 * grp;
+            const int blk = tok < L ? lane_blk(c) : -1;
+            const int b = blk >= 0 ? blk : 0;
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd) {
+                const int d = 16 * (2 * wave + dd) + col;
+                vv[c][dd] = ld16(vc + (((int64_t)b * Hkv + g) * kD + d) * kBlock + (tok & 15));
+            }
+        }
+        // this wave's q and K loads have landed (only the kVLoads value loads,
+        // issued after them, may still fly); then every wave's K has
+        __builtin_amdgcn_s_waitcnt((kVLoads & 0xF) | ((kVLoads >> 4) << 14) | (0x7 << 4));
+        asm volatile("s_barrier" ::: "memory");
+        bf16x8 qf[4];
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc) qf[dc] = as_bf16x8(qok ? qraw[dc] : zero_u32x4());
 
         // scores of chunks 2*wave, 2*wave+1
         float sv[2][8];
@@ -199,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
             for (int j = 0; j < 8; ++j) mx = fmaxf(mx, sv[cc][j]);
         mx = colmax_finish(mx);
         if (grp == 0) s_max[wave][col] = mx;
-        __syncthreads();
+        lds_barrier();
         const float m = fmaxf(fmaxf(s_max[0][col], s_max[1][col]), fmaxf(s_max[2][col], s_max[3][col]));
 
         // bf16 weights -> LDS as P^T[q][token]
@@ -213,7 +240,23 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
                 wv[j] = weight_f32(sv[cc][j], m, whole || (blk_ok && (t0 + 32 * c + 8 * grp + j) < L));
             st16(&s_pt[col * kPtStride + 32 * c + 8 * grp], as_u32x4(pack_weights(wv)));
         }
-        __syncthreads();
+        lds_barrier();
+
+        // the value operands have landed; zero the slots of tokens past the
+        // sequence or in a block outside the pool
+        __builtin_amdgcn_s_waitcnt(0x0070);                      // vmcnt(0)
+        if (!whole) {
+#pragma unroll
+            for (int c = 0; c < kChunks; ++c) {
+                const int tok = t0 + 32 * c + 8 * grp;
+                const bool ok = tok < L && lane_blk(c) >= 0;
+#pragma unroll
+                for (int dd = 0; dd < 2; ++dd) {
+                    if (!ok) vv[c][dd] = zero_u32x4();
+                    else if (tok + 8 > L) vv[c][dd] = keep_first(vv[c][dd], L - tok);
+                }
+            }
+        }
 
         // values chain over the whole split for head-dim tiles 2*wave, 2*wave+1
         f32x4 o[2];
@@ -231,17 +274,29 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 
         if (col < G) {
             const int h = g * G + col;
-            float* base = ws + (((int64_t)s * Hq + h) * max_splits + i) * (kD + 2);
+            if (t0 == 0 && Lseq <= split_len) {
+                // the sequence's only split: its fold is the split itself, so
+                // the output is o / l, rounded, exactly what the combine would write
+                uint16_t* orow = out + (int64_t)s * ldo + (int64_t)h * kD;
 #pragma unroll
-            for (int dd = 0; dd < 2; ++dd)
+                for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) base[2 + 16 * (2 * wave + dd) + 4 * grp + r] = o[dd][r];
-            if (wave == 0 && grp == 0) {
-                base[0] = m;
-                base[1] = ls;
+                    for (int r = 0; r < 4; ++r)
+                        orow[16 * (2 * wave + dd) + 4 * grp + r] =
+                            (uint16_t)f32_to_bf16_rne(finish_value(o[dd][r], ls));
+            } else {
+                float* base = ws + (((int64_t)s * Hq + h) * max_splits + i) * (kD + 2);
+#pragma unroll
+                for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) base[2 + 16 * (2 * wave + dd) + 4 * grp + r] = o[dd][r];
+                if (wave == 0 && grp == 0) {
+                    base[0] = m;
+                    base[1] = ls;
+                }
             }
         }
-        __syncthreads();   // s_max / s_pt are reused by the next item
+        lds_barrier();     // s_max / s_pt / s_blk are reused by the next item
     }
 }
 
@@ -277,6 +332,7 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
         *o = 0;
         return;
     }
+    if (n == 1) return;            // written by the split kernel
     const float* base = ws + ((int64_t)s * Hq + h) * max_splits * (kD + 2);
     float Mprev = -INFINITY, Lam = 0.f, O = 0.f;
     for (int c0 = 0; c0 < n; c0 += kFoldChunk) {
@@ -403,7 +459,7 @@ static inline int decode_launch(const void* q, int64_t ldq, const void* k_cache,
     hipLaunchKernelGGL(decode_split_kernel, dim3(P, Hkv), dim3(kThreads), 0, st,
                        (const uint16_t*)q, ldq, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
                        num_blocks, block_table, max_blocks, kv_lens, S, Hq, Hkv, max_splits, split_len,
-                       scale_log2, (float*)ws);
+                       scale_log2, (float*)ws, (uint16_t*)out, ldo);
     int rc = bi_launch_status();
     if (rc != BI_OK) return rc;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(Hq, S), dim3(kD), 0, st, (const float*)ws,
