@@ -133,8 +133,13 @@ int bi_kv_append(const void* k_new, const void* v_new, int64_t ld_new, const int
                  int32_t Hkv, int32_t D, void* stream);
 
 /*
- * Workspace for bi_attention_decode: S * Hq * ceil(max_kv_len/256) split
- * partials of (D + 2) floats each.
+ * Workspace for bi_attention_decode, laid out from its first 256-byte
+ * boundary: 256 bytes for the work counter of the split kernel (zeroed by the
+ * call itself, with a kernel, on its stream), then per split and query head a
+ * row of D fp32 partial values, then 128 bytes per split and KV head for the
+ * partial (max, sum) pairs (sized for Hkv == Hq, which needs the most).  Every
+ * partial line is written whole by one wavefront.  Size: 255 + 256 +
+ * S * Hq * ceil(max_kv_len/256) * (D + 32) * 4 bytes.
  */
 size_t bi_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D, int32_t max_kv_len);
 
@@ -157,9 +162,13 @@ size_t bi_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D, int32_t ma
  * in the attention (score -inf, value 0), here and in bi_attention_prefill
  * alike, so such a row still does not depend on the rest of the batch (a row
  * with no token left gets 0/0 = NaN).
- * ws: device workspace of at least bi_attention_workspace_bytes(S, Hq, D, max_kv_len).
- * Requires D == 128, Hq % Hkv == 0, Hq/Hkv <= 16, 1 <= max_kv_len <= 1<<20,
- * S <= 2048, 16-byte aligned q/out/caches, ldq/ldo % 8 == 0.
+ * ws: device workspace of at least bi_attention_workspace_bytes(S, Hq, D, max_kv_len);
+ * its contents need no initialisation, and calls that share one ws must not
+ * overlap in time.  Which workgroup computes which split is decided at run
+ * time (a work counter), and has no influence on any result.
+ * Requires D == 128, Hq % Hkv == 0, Hq/Hkv <= 16, Hkv <= 256,
+ * 1 <= max_kv_len <= 1<<20, S <= 2048, S * ceil(max_kv_len/256) * Hkv <= 2^30
+ * (else BI_ERR_UNSUPPORTED), 16-byte aligned q/out/caches, ldq/ldo % 8 == 0.
  */
 int bi_attention_decode(const void* q, int64_t ldq, const void* k_cache, const void* v_cache,
                         int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
@@ -176,11 +185,12 @@ int bi_attention_decode(const void* q, int64_t ldq, const void* k_cache, const v
  * call never allocates or frees memory (neither does the rest of the library).
  * Limit: bi_attention_workspace_bytes(S, Hq, D, max_kv_len) must not exceed
  * BI_ATTENTION_DECODE_NOALLOC_SCRATCH_BYTES (64 MiB; e.g. S * Hq *
- * ceil(max_kv_len/256) <= 129055 for D = 128), else BI_ERR_WORKSPACE_TOO_SMALL
+ * ceil(max_kv_len/256) <= 104856 for D = 128), else BI_ERR_WORKSPACE_TOO_SMALL
  * is returned before any device work.  Every call on one GPU shares that GPU's
  * array: calls that overlap in time on one GPU (other streams, other host
  * threads) race and must be serialised by the caller.  Nothing needs clearing
- * between calls.
+ * between calls (each call zeroes the array's work counter itself, with a
+ * kernel on its stream).
  */
 #define BI_ATTENTION_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int bi_attention_decode_noalloc(const void* q, int64_t ldq, const void* k_cache, const void* v_cache,

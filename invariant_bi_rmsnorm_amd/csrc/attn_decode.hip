@@ -6,12 +6,19 @@
 // split SIZE, so the split boundaries of a sequence never move with the batch,
 // the length mix or the number of sequences.
 //
-// Two kernels:
-//  1. decode_split_kernel: persistent workgroups over the work list of
-//     (sequence, split) pairs, one KV head per grid row.  Each workgroup first
-//     builds the prefix of split counts ceil(kv_len/256) of all sequences in
-//     LDS (integer, exact), then takes items blockIdx.x, blockIdx.x + gridDim.x,
-//     ...  Which workgroup computes an item has no influence on its arithmetic.
+// Three kernels:
+//  0. decode_ticket_reset zeroes the work counter at the head of the workspace.
+//  1. decode_split_kernel: persistent workgroups (as many as fit on the GPU at
+//     once) over the work list of (sequence, split, KV head) items.  Each
+//     workgroup first builds the prefix of split counts ceil(kv_len/256) of
+//     all sequences in LDS (integer, exact), then takes two items by its index
+//     and the rest from the counter, so faster workgroups take more items and
+//     the grid drains together.  Which workgroup computes an item has no
+//     influence on its arithmetic.  The next item's length and block ids are
+//     loaded while the current one is computed; an item's results leave in
+//     one store instruction per wavefront (gathered across lanes), issued
+//     after the next item's value loads so that no wait covers it; the KV
+//     cache is read with non-temporal loads.
 //     Per item: 4 wavefronts each score 64 of the split's 256 tokens for the
 //     (up to 16) query heads of the KV group, the split max is taken across
 //     the waves, the bf16 weights go to LDS as P^T, and each wave then runs
@@ -55,8 +62,9 @@ extern "C" int bi_attention_decode(const void* q, int64_t ldq, const void* k_cac
 // address, until the process ends.  The array's name is a host-side stand-in:
 // host code only ever passes the address hipGetSymbolAddress returns for the
 // current device.  The partials of a call are all written by its split kernel
-// before its combine kernel reads them, so nothing has to be cleared between
-// calls; calls that overlap on one GPU share the array and race.
+// before its combine kernel reads them, and the work counter at the array's
+// head is zeroed by the call's first kernel, so nothing has to be cleared
+// between calls; calls that overlap on one GPU share the array and race.
 constexpr size_t kNoAllocScratchBytes = BI_ATTENTION_DECODE_NOALLOC_SCRATCH_BYTES;
 constexpr int kNoAllocMaxDevices = 64;
 static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];

@@ -15,6 +15,9 @@ constexpr int kMaxSeqs = 2048;
 // reads and writes of one wavefront free of LDS bank conflicts on gfx950
 // (a 16-byte pad costs 4 conflict cycles per access there)
 constexpr int kPtStride = kSplit + 16;
+// floats per item in the (m, l) region: one 128-byte line, the pairs of up to
+// 16 query columns
+constexpr int kMlFloats = 32;
 static_assert(16 * kPtStride <= kSplit * kD, "P^T fits in the K buffer it aliases");
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
@@ -42,6 +45,12 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_barrier" ::: "memory");
 }
 
+// The KV cache is read once per call, so its loads are marked non-temporal
+// (cache policy NT; for the LDS-DMA builtin the policy argument): streamed
+// through, they do not push the split partials out of L2 and the MALL, which
+// measured 6 % faster at 256 sequences of up to 32K tokens.
+constexpr int kStreamPolicy = 2;
+
 // loads issued per lane per item for the values operands (all unconditional,
 // so the count is fixed: the wait for K below leaves exactly these in flight)
 constexpr int kVLoads = 2 * kChunks;
@@ -51,17 +60,17 @@ constexpr int kVLoads = 2 * kChunks;
 // touches fall in distinct banks.
 __device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
 
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t num_blocks, const int32_t* __restrict__ bt,
     int max_blocks, const int32_t* __restrict__ kv_lens, int S, int Hq, int Hkv,
-    int max_splits, int split_len, float scale_log2, float* __restrict__ ws, uint16_t* __restrict__ out,
-    int64_t ldo)
+    int max_splits, int split_len, float scale_log2, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    uint16_t* __restrict__ out, int64_t ldo, unsigned* __restrict__ tickets)
 {
     __shared__ int s_off[kMaxSeqs + 1];
     __shared__ int s_part[kThreads];
     __shared__ float s_max[4][16];
-    __shared__ int s_blk[kSplit / kBlock];
+    __shared__ int s_ticket;
     // K of the split [256][128] bf16; after the scores it holds P^T [16][kPtStride]
     __shared__ __attribute__((aligned(1024))) uint16_t s_k[kSplit * kD];
     uint16_t* const s_pt = s_k;
@@ -71,7 +80,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const int wave = tid >> 6;
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int g = blockIdx.y;
     const int G = Hq / Hkv;
     const int cap = min(max_blocks * kBlock, max_splits * split_len);
 
@@ -102,38 +110,191 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     if (tid == kThreads - 1) s_off[S] = s_part[kThreads - 1];
     __syncthreads();
     const int total = s_off[S];
+    // work items are (split, KV head) pairs, ticket t = item * Hkv + head:
+    // a workgroup takes tickets blockIdx.x and blockIdx.x + gridDim.x, then
+    // draws 2 gridDim.x + (a counter the host zeroes before the launch), so
+    // the workgroups that run faster take more items and all finish together
+    const int n_tickets = total * Hkv;
+    const int P = (int)gridDim.x;
+    if ((int)blockIdx.x >= n_tickets) return;      // uniform over the workgroup
 
-    for (int w = blockIdx.x; w < total; w += gridDim.x) {
-        // sequence of item w: the largest s with s_off[s] <= w
+    // sequence and split index of item w: the largest s with s_off[s] <= w
+    auto locate = [&](int w, int& s_, int& i_) __attribute__((always_inline)) {
         int lo = 0, hi = S - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (s_off[mid] <= w) lo = mid; else hi = mid - 1;
         }
-        const int s = lo;
-        const int i = w - s_off[s];
-        const int Lseq = clamp_len(kv_lens[s], cap);
+        s_ = lo;
+        i_ = w - s_off[lo];
+    };
+    // every lane loads the sequence length and the table entry of block
+    // (lane & 15) of an item (16 blocks of 16 tokens cover a split); entries
+    // past the sequence are read from inside the table row and masked later
+    auto raw_len = [&](int s_) __attribute__((always_inline)) { return kv_lens[s_]; };
+    auto raw_blk = [&](int s_, int i_) __attribute__((always_inline)) {
+        const int b = min(((i_ * split_len) >> 4) + (tid & 15), max_blocks - 1);
+        return bt[(int64_t)s_ * max_blocks + b];
+    };
+
+    // physical block of this lane's block (lane & 15) of the split starting at
+    // token t0_: -1 where the block holds no token of the split or its id is
+    // outside the pool.  Tokens of such a block do not exist for the
+    // arithmetic (score -inf, weight 0, value 0; their K rows are never
+    // loaded, so nothing stale from an earlier item can reach the result).
+    auto lane_block = [&](int t0_, int Lseq_, int blk_raw) __attribute__((always_inline)) {
+        const int L_ = min(Lseq_, t0_ + split_len);
+        return (t0_ + kBlock * (tid & 15) < L_ && blk_raw >= 0 && blk_raw < num_blocks) ? blk_raw : -1;
+    };
+
+    // an item's length and block ids are loaded one item ahead (and taken
+    // from registers after the wait for the previous item's values), and its
+    // sequence is located two items ahead, so no item starts with a wait on
+    // global memory
+    // Results leave in as few store instructions as possible: each store
+    // instruction holds up the CU's memory pipeline far longer than its bytes
+    // take, so a wave gathers its values with cross-lane reads into one
+    // full-width store (two or three for more than 7 query heads per KV head).
+    // Lane (col, grp) holds dims 16 (2 wave + dd) + 4 grp + r of query column
+    // col.  Every partial line is written whole by one wavefront (lines
+    // written in part at different times cost HBM more).  The first store's
+    // data and addresses are returned (it is issued later, with every lane
+    // on: lanes without a value of their own repeat another lane's value and
+    // address, so no branch makes the number of store instructions vary); any
+    // other store is issued here.
+    auto store_prepare = [&](const f32x4 (&o_)[2], float ls_, float m_, int s_, int i_, int g_, bool single,
+                             u32x4& st_v, uint32_t*& st_p) __attribute__((always_inline)) {
+        if (single) {
+            // the sequence's only split: its fold is the split itself, so the
+            // output is o / l, rounded, exactly what the combine would write.
+            // Store lane t = 4 hh + j (hh < G): dims 32 wave + 8 j .. + 7 of
+            // head g G + hh, from lanes (hh, 2 (j & 1)) and (hh, 2 (j & 1) + 1),
+            // values dd = j >> 1.  (A shuffle reads the source lane's value:
+            // both candidates are read and the destination lane picks.)
+            u32x4 pk;                                   // this lane's 8 values, rounded
+            pk[0] = pack_bf16x2(finish_value(o_[0][0], ls_), finish_value(o_[0][1], ls_));
+            pk[1] = pack_bf16x2(finish_value(o_[0][2], ls_), finish_value(o_[0][3], ls_));
+            pk[2] = pack_bf16x2(finish_value(o_[1][0], ls_), finish_value(o_[1][1], ls_));
+            pk[3] = pack_bf16x2(finish_value(o_[1][2], ls_), finish_value(o_[1][3], ls_));
+            const int t = lane % (4 * G);                // 4 G <= 64 lanes carry values
+            const int hh = t >> 2;
+            const int j = t & 3;
+            const int srcA = hh + 16 * (2 * (j & 1));
+            const int srcB = srcA + 16;
+            const bool hi = (j >> 1) != 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t a0 = (uint32_t)__shfl((int)pk[e], srcA, 64);
+                const uint32_t a1 = (uint32_t)__shfl((int)pk[2 + e], srcA, 64);
+                const uint32_t b0 = (uint32_t)__shfl((int)pk[e], srcB, 64);
+                const uint32_t b1 = (uint32_t)__shfl((int)pk[2 + e], srcB, 64);
+                st_v[e] = hi ? a1 : a0;
+                st_v[2 + e] = hi ? b1 : b0;
+            }
+            st_p = (uint32_t*)(out + (int64_t)s_ * ldo + (int64_t)(g_ * G + hh) * kD + 32 * wave + 8 * j);
+            return;
+        }
+        // o rows: store lane t = 8 hh + j (hh < G) writes dims 32 wave + 4 j
+        // .. + 3 of head g G + hh, from lane (hh, j & 3), values dd = j >> 2;
+        // on wave 0 the 8 lanes after them (when G <= 7) write the item's
+        // (m, l) line: lane 8 G + k holds the pairs of columns 2k, 2k + 1
+        const int n_o = 8 * G;
+        const bool ml_inline = n_o + 8 <= 64;
+        float* const mrow = ws_ml + (((int64_t)s_ * Hkv + g_) * max_splits + i_) * kMlFloats;
+        // lanes of the first store without a value: lane l repeats lane
+        // l mod n_store (n_store = the lanes with values)
+        const int n_store = min(64, ml_inline && wave == 0 ? n_o + 8 : n_o);
+        for (int base = 0; base < n_o; base += 64) {          // one pass while G <= 8
+            const int t = base == 0 ? lane % n_store : base + lane;
+            const int hh = (t >> 3) & 15;
+            const int j = t & 7;
+            const int src = hh + 16 * (j & 3);
+            const bool hi = (j >> 2) != 0;
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v0 = __shfl(o_[0][r], src, 64);
+                const float v1 = __shfl(o_[1][r], src, 64);
+                v[r] = hi ? v1 : v0;
+            }
+            float* dst = ws_o + (((int64_t)s_ * Hq + g_ * G + hh) * max_splits + i_) * kD + 32 * wave + 4 * j;
+            const bool on = t < n_o;
+            if (base == 0 && ml_inline && wave == 0) {
+                const int k = (t - n_o) & 7;
+                f32x4 ml;
+                ml[0] = __shfl(m_, 2 * k, 64);
+                ml[1] = __shfl(ls_, 2 * k, 64);
+                ml[2] = __shfl(m_, 2 * k + 1, 64);
+                ml[3] = __shfl(ls_, 2 * k + 1, 64);
+                if (!on) {
+                    v = ml;
+                    dst = mrow + 4 * k;
+                }
+            }
+            if (base == 0) {
+                st_v = __builtin_bit_cast(u32x4, v);
+                st_p = (uint32_t*)dst;
+            } else if (on) {
+                *reinterpret_cast<f32x4*>(dst) = v;
+            }
+        }
+        if (!ml_inline && wave == 0 && grp == 0) {
+            f32x2_t ml;
+            ml[0] = m_;
+            ml[1] = ls_;
+            *reinterpret_cast<f32x2_t*>(mrow + 2 * col) = ml;
+        }
+    };
+
+    // An item's first store is issued after the next item's value loads, so
+    // no counted wait of the wave waits for a fresh store (a store counts in
+    // vmcnt like a load, and under load its completion comes back late): the
+    // K wait allows the value loads and that one store to be in flight, the
+    // value wait the store.  Every iteration issues exactly that one store
+    // instruction; before the first item it writes zeros into the spare
+    // second half of the ticket line.
+    u32x4 st_v = {0u, 0u, 0u, 0u};
+    uint32_t* st_p = (uint32_t*)((char*)tickets + 128 + 16 * (lane & 7));
+
+    // sequence, split and KV head of ticket t (tickets past the last read the
+    // last item's entries: their loads stay in bounds and are never used)
+    auto ticket_item = [&](int t, int& s_, int& i_, int& g_) __attribute__((always_inline)) {
+        const int tc = min(t, n_tickets - 1);
+        const int item = tc / Hkv;
+        g_ = tc - item * Hkv;
+        locate(item, s_, i_);
+    };
+    int t_cur = blockIdx.x, t_next = blockIdx.x + P;
+    int cs, ci, cg, ns, ni, ng;
+    ticket_item(t_cur, cs, ci, cg);
+    int c_Lseq = clamp_len(raw_len(cs), cap);
+    int c_blk = lane_block(ci * split_len, c_Lseq, raw_blk(cs, ci));
+    ticket_item(t_next, ns, ni, ng);
+
+    while (t_cur < n_tickets) {
+        // loads of the next item, and the ticket of the one after, issued
+        // ahead of this item's operand loads
+        const int n_len = raw_len(ns);
+        const int n_blk = raw_blk(ns, ni);
+        // (an increment-with-wrap at 2^32 - 1 is a plain increment; unlike an
+        // add it is issued as one atomic whose result is waited for only where
+        // it is used)
+        unsigned drawn = 0;
+        if (tid == 0) drawn = __builtin_amdgcn_atomic_inc32(tickets, 0xffffffffu, __ATOMIC_RELAXED, "agent");
+        asm volatile("" ::: "memory");
+
+        const int s = cs;
+        const int i = ci;
+        const int g = cg;
+        const int Lseq = c_Lseq;
         const int t0 = i * split_len;
         // tokens of this split: [t0, L); with split_len == 256 (the library's
         // only value) L is the sequence length
         const int L = min(Lseq, t0 + split_len);
-        const int32_t* btr = bt + (int64_t)s * max_blocks;
-
-        // physical blocks of the split's 16 cache blocks (-1: none / invalid)
-        if (tid < kSplit / kBlock) {
-            const int tok = t0 + kBlock * tid;
-            int blk = -1;
-            if (tok < L) blk = btr[tok >> 4];
-            s_blk[tid] = (blk >= 0 && blk < num_blocks) ? blk : -1;
-        }
-        lds_barrier();
-
-        // tokens of a block whose id is outside the pool do not exist for the
-        // arithmetic: score -inf, weight 0, value 0 (their K rows are never
-        // loaded, so nothing stale from an earlier item can reach the result)
-        int blk16[kSplit / kBlock];                  // the 16 ids in registers (broadcast reads, once)
+        const int my_blk = c_blk;
+        int blk16[kSplit / kBlock];                  // the 16 ids, wave-uniform
 #pragma unroll
-        for (int b = 0; b < kSplit / kBlock; ++b) blk16[b] = s_blk[b];
+        for (int b = 0; b < kSplit / kBlock; ++b) blk16[b] = __builtin_amdgcn_readlane(my_blk, b);
         // block of this lane's tokens 32 c + 8 grp .. + 7 (blk16[2c] or blk16[2c+1]),
         // chosen with bit operations so the array is never indexed per lane
         const int hi_mask = -(grp >> 1);
@@ -168,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
                 const int gch = (lane & 15) ^ kswz(row);         // chunk landing at slot lane&15
                 __builtin_amdgcn_global_load_lds(
                     kc + (((int64_t)blk * Hkv + g) * kBlock + (tok & 15)) * kD + gch * 8,
-                    s_k + inst * 512, 16, 0, 0);
+                    s_k + inst * 512, 16, 0, kStreamPolicy);
             }
         }
 
@@ -184,16 +345,30 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
             for (int dd = 0; dd < 2; ++dd) {
                 const int d = 16 * (2 * wave + dd) + col;
-                vv[c][dd] = ld16(vc + (((int64_t)b * Hkv + g) * kD + d) * kBlock + (tok & 15));
+                vv[c][dd] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(vc + (((int64_t)b * Hkv + g) * kD + d) * kBlock + (tok & 15)));
             }
         }
-        // this wave's q and K loads have landed (only the kVLoads value loads,
-        // issued after them, may still fly); then every wave's K has
-        __builtin_amdgcn_s_waitcnt((kVLoads & 0xF) | ((kVLoads >> 4) << 14) | (0x7 << 4));
+        __builtin_nontemporal_store(st_v, reinterpret_cast<u32x4*>(st_p));
+
+        // this wave's q and K loads have landed (only the kVLoads value loads
+        // and the store issued after them may still fly); then every wave's K has
+        constexpr int kW1 = kVLoads + 1;
+        __builtin_amdgcn_s_waitcnt((kW1 & 0xF) | ((kW1 >> 4) << 14) | (0x7 << 4));
         asm volatile("s_barrier" ::: "memory");
+        // (the ticket drawn above has landed with the q and K loads; the other
+        // waves read it after the next barrier)
+        if (tid == 0) s_ticket = 2 * P + (int)drawn;
         bf16x8 qf[4];
 #pragma unroll
         for (int dc = 0; dc < 4; ++dc) qf[dc] = as_bf16x8(qok ? qraw[dc] : zero_u32x4());
+
+        // block of tokens 32 c + 8 grp .. + 7 for the two chunks c = 2 wave + cc
+        // this wave scores (a lane read across the wave, no LDS round trip)
+        bool blk_ok[2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+            blk_ok[cc] = whole || __shfl(my_blk, 2 * (2 * wave + cc) + (grp >> 1), 64) >= 0;
 
         // scores of chunks 2*wave, 2*wave+1
         float sv[2][8];
@@ -208,11 +383,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
                 for (int dc = 0; dc < 4; ++dc)
                     kf[dc] = *reinterpret_cast<const bf16x8*>(s_k + row * kD + (((4 * dc + grp) ^ kswz(row)) * 8));
                 const f32x4 acc = score_tile(kf, qf);
-                const bool blk_ok = whole || s_blk[2 * c + (grp >> 1)] >= 0;   // block of tokens 8 grp .. 8 grp + 7
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = 4 * h + r;
-                    const bool valid = whole || (blk_ok && (t0 + 32 * c + 8 * grp + j) < L);
+                    const bool valid = whole || (blk_ok[cc] && (t0 + 32 * c + 8 * grp + j) < L);
                     sv[cc][j] = valid ? scaled_score(acc[r], scale_log2) : -INFINITY;
                 }
             }
@@ -228,23 +402,28 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         if (grp == 0) s_max[wave][col] = mx;
         lds_barrier();
         const float m = fmaxf(fmaxf(s_max[0][col], s_max[1][col]), fmaxf(s_max[2][col], s_max[3][col]));
+        const int t_after = s_ticket;
+        int s2, i2, g2;
+        ticket_item(t_after, s2, i2, g2);
 
         // bf16 weights -> LDS as P^T[q][token]
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             const int c = 2 * wave + cc;
-            const bool blk_ok = whole || s_blk[2 * c + (grp >> 1)] >= 0;
             float wv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                wv[j] = weight_f32(sv[cc][j], m, whole || (blk_ok && (t0 + 32 * c + 8 * grp + j) < L));
+                wv[j] = weight_f32(sv[cc][j], m, whole || (blk_ok[cc] && (t0 + 32 * c + 8 * grp + j) < L));
             st16(&s_pt[col * kPtStride + 32 * c + 8 * grp], as_u32x4(pack_weights(wv)));
         }
         lds_barrier();
 
         // the value operands have landed; zero the slots of tokens past the
         // sequence or in a block outside the pool
-        __builtin_amdgcn_s_waitcnt(0x0070);                      // vmcnt(0)
+        __builtin_amdgcn_s_waitcnt(0x0071);                      // vmcnt(1): the store may fly
+        // (the next item's loads, issued before this item's, have landed too)
+        const int n_Lseq = clamp_len(n_len, cap);
+        const int n_myblk = lane_block(ni * split_len, n_Lseq, n_blk);
         if (!whole) {
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
@@ -272,32 +451,28 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         }
         ls = lsum_finish(ls);
 
-        if (col < G) {
-            const int h = g * G + col;
-            if (t0 == 0 && Lseq <= split_len) {
-                // the sequence's only split: its fold is the split itself, so
-                // the output is o / l, rounded, exactly what the combine would write
-                uint16_t* orow = out + (int64_t)s * ldo + (int64_t)h * kD;
-#pragma unroll
-                for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        orow[16 * (2 * wave + dd) + 4 * grp + r] =
-                            (uint16_t)f32_to_bf16_rne(finish_value(o[dd][r], ls));
-            } else {
-                float* base = ws + (((int64_t)s * Hq + h) * max_splits + i) * (kD + 2);
-#pragma unroll
-                for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) base[2 + 16 * (2 * wave + dd) + 4 * grp + r] = o[dd][r];
-                if (wave == 0 && grp == 0) {
-                    base[0] = m;
-                    base[1] = ls;
-                }
-            }
-        }
-        lds_barrier();     // s_max / s_pt / s_blk are reused by the next item
+        store_prepare(o, ls, m, s, i, g, t0 == 0 && Lseq <= split_len, st_v, st_p);
+        lds_barrier();     // s_max / s_pt are reused by the next item
+        c_Lseq = n_Lseq;
+        c_blk = n_myblk;
+        t_cur = t_next;
+        t_next = t_after;
+        cs = ns;
+        ci = ni;
+        cg = ng;
+        ns = s2;
+        ni = i2;
+        ng = g2;
     }
+    *reinterpret_cast<u32x4*>(st_p) = st_v;
+}
+
+// Zeroes the split kernel's ticket counter (a kernel rather than a memset, so
+// the launch sequence can be captured in a HIP graph and replayed).
+constexpr size_t kTicketBytes = 256;
+__global__ void decode_ticket_reset(unsigned* tickets)
+{
+    if (threadIdx.x == 0) *tickets = 0u;
 }
 
 // Fold of the split partials of one (sequence, query head), 128 threads (one
@@ -316,8 +491,8 @@ constexpr int kFoldChunk = kD;
 constexpr int kPre = 32;
 
 __global__ __launch_bounds__(kD) void decode_combine_kernel(
-    const float* __restrict__ ws, const int32_t* __restrict__ kv_lens, int cap, int Hq,
-    int max_splits, int split_len, uint16_t* __restrict__ out, int64_t ldo)
+    const float* __restrict__ ws_o, const float* __restrict__ ws_ml, const int32_t* __restrict__ kv_lens,
+    int cap, int Hq, int Hkv, int max_splits, int split_len, uint16_t* __restrict__ out, int64_t ldo)
 {
     __shared__ float s_a[kFoldChunk], s_b[kFoldChunk], s_l[kFoldChunk];
     __shared__ float s_wmax[2];
@@ -333,18 +508,22 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
         return;
     }
     if (n == 1) return;            // written by the split kernel
-    const float* base = ws + ((int64_t)s * Hq + h) * max_splits * (kD + 2);
+    const int G = Hq / Hkv;
+    const int g = h / G;
+    const float* base = ws_o + ((int64_t)s * Hq + h) * max_splits * kD;
+    const float* mlb = ws_ml + ((int64_t)s * Hkv + g) * max_splits * kMlFloats + 2 * (h - g * G);
     float Mprev = -INFINITY, Lam = 0.f, O = 0.f;
     for (int c0 = 0; c0 < n; c0 += kFoldChunk) {
         const int cn = min(kFoldChunk, n - c0);
-        const float* cb = base + (int64_t)c0 * (kD + 2);
+        const float* cb = base + (int64_t)c0 * kD;
         // ---- scalar part: thread d owns split c0 + d
         const bool own = d < cn;
-        const float mi = own ? cb[(int64_t)d * (kD + 2)] : -INFINITY;
-        const float li = own ? cb[(int64_t)d * (kD + 2) + 1] : 0.f;
+        const float* ml = mlb + (int64_t)(c0 + d) * kMlFloats;
+        const float mi = own ? ml[0] : -INFINITY;
+        const float li = own ? ml[1] : 0.f;
         float v[kPre];
 #pragma unroll
-        for (int j = 0; j < kPre; ++j) v[j] = j < cn ? cb[(int64_t)j * (kD + 2) + 2 + d] : 0.f;
+        for (int j = 0; j < kPre; ++j) v[j] = j < cn ? cb[(int64_t)j * kD + d] : 0.f;
         float run = mi;                                   // inclusive prefix max inside the wave
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -370,7 +549,7 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
             if (i0 > 0) {
 #pragma unroll
                 for (int j = 0; j < kPre; ++j)
-                    v[j] = i0 + j < cn ? cb[(int64_t)(i0 + j) * (kD + 2) + 2 + d] : 0.f;
+                    v[j] = i0 + j < cn ? cb[(int64_t)(i0 + j) * kD + d] : 0.f;
             }
 #pragma unroll
             for (int j = 0; j < kPre; ++j) {
@@ -394,12 +573,32 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
 
 static inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Workspace of split partials when splits are `split_len` tokens long.
+// Workspace when splits are `split_len` tokens long, from the first 256-byte
+// boundary in it: the ticket counter of the split kernel (kTicketBytes), the o
+// rows [S][Hq][splits][D] fp32, then one (m, l) line of kMlFloats per
+// (sequence, KV head, split) item.  The host sizes the (m, l) region for
+// Hkv == Hq (the size query takes no Hkv); Hkv < Hq uses less of it.
 static inline size_t decode_ws_bytes(int32_t S, int32_t Hq, int32_t D, int32_t max_kv_len, int split_len)
 {
     if (S <= 0 || Hq <= 0 || D <= 0 || max_kv_len <= 0) return 0;
-    return (size_t)S * (size_t)Hq * (size_t)ceil_div64(max_kv_len, split_len) * (size_t)(D + 2) *
-           sizeof(float);
+    const size_t rows = (size_t)S * (size_t)Hq * (size_t)ceil_div64(max_kv_len, split_len);
+    return 255 + kTicketBytes + rows * ((size_t)D + kMlFloats) * sizeof(float);
+}
+
+struct DecodeWs {
+    unsigned* tickets;
+    float* o;
+    float* ml;
+};
+
+static inline DecodeWs decode_ws_layout(void* ws, int32_t S, int32_t Hq, int max_splits)
+{
+    char* a = (char*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
+    DecodeWs w;
+    w.tickets = (unsigned*)a;
+    w.o = (float*)(a + kTicketBytes);
+    w.ml = w.o + (size_t)S * Hq * max_splits * kD;
+    return w;
 }
 
 // Host validation shared by every bi_attention_decode build: BI_OK to go on,
@@ -424,7 +623,7 @@ static inline int decode_validate(const void* q, int64_t ldq, const void* k_cach
                   !bi_aligned(out, 2) || (caller_ws && !bi_aligned(ws, 16)) || !bi_aligned(block_table, 4) ||
                   !bi_aligned(kv_lens, 4)))
         return BI_ERR_INVALID_ARGUMENT;
-    if (D != kD || Hq / Hkv > 16 || S > kMaxSeqs || max_kv_len > (1 << 20) || Hkv > 65535)
+    if (D != kD || Hq / Hkv > 16 || S > kMaxSeqs || max_kv_len > (1 << 20) || Hkv > 256)
         return BI_ERR_UNSUPPORTED;
     if (S == 0) return -1;
     return BI_OK;
@@ -440,6 +639,9 @@ static inline int decode_launch(const void* q, int64_t ldq, const void* k_cache,
 {
     const int max_splits = (int)ceil_div64(max_kv_len, split_len);
     const int64_t items_bound = (int64_t)S * max_splits;
+    // tickets (and the counter's draws past them) stay far inside int range;
+    // checked before any device call
+    if (items_bound * Hkv > ((int64_t)1 << 30)) return BI_ERR_UNSUPPORTED;
     // persistent grid: as many workgroups as can be resident at once (a
     // second, partial round of workgroups would run at low occupancy)
     static const int resident = [] {
@@ -452,19 +654,22 @@ static inline int decode_launch(const void* q, int64_t ldq, const void* k_cache,
             return 1024;
         return cus * per_cu;
     }();
-    const int64_t per_head = std::max<int64_t>(1, resident / Hkv);
-    const int P = (int)std::min<int64_t>(items_bound, per_head);
+    const int P = (int)std::min<int64_t>(items_bound * Hkv, resident);
     const float scale_log2 = scale_log2_of(scale);
     hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL(decode_split_kernel, dim3(P, Hkv), dim3(kThreads), 0, st,
-                       (const uint16_t*)q, ldq, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
-                       num_blocks, block_table, max_blocks, kv_lens, S, Hq, Hkv, max_splits, split_len,
-                       scale_log2, (float*)ws, (uint16_t*)out, ldo);
+    const DecodeWs w = decode_ws_layout(ws, S, Hq, max_splits);
+    hipLaunchKernelGGL(decode_ticket_reset, dim3(1), dim3(64), 0, st, w.tickets);
     int rc = bi_launch_status();
     if (rc != BI_OK) return rc;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(Hq, S), dim3(kD), 0, st, (const float*)ws,
-                       kv_lens, std::min(max_blocks * kBlock, max_splits * split_len), Hq, max_splits,
-                       split_len, (uint16_t*)out, ldo);
+    hipLaunchKernelGGL(decode_split_kernel, dim3(P), dim3(kThreads), 0, st,
+                       (const uint16_t*)q, ldq, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
+                       num_blocks, block_table, max_blocks, kv_lens, S, Hq, Hkv, max_splits, split_len,
+                       scale_log2, w.o, w.ml, (uint16_t*)out, ldo, w.tickets);
+    rc = bi_launch_status();
+    if (rc != BI_OK) return rc;
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(Hq, S), dim3(kD), 0, st, (const float*)w.o,
+                       (const float*)w.ml, kv_lens, std::min(max_blocks * kBlock, max_splits * split_len), Hq,
+                       Hkv, max_splits, split_len, (uint16_t*)out, ldo);
     return bi_launch_status();
 }
 

@@ -121,7 +121,9 @@ def test_kv_append_validation(L):
 
 def test_attention_validation(L):
     ws = L.bi_attention_workspace_bytes(4, 32, 128, 1000)
-    assert ws == 4 * 32 * 4 * 130 * 4
+    # alignment slack, work counter, then per split and query head a 128-float o
+    # row and (for Hkv == Hq, the bound) a 32-float (m, l) line
+    assert ws == 255 + 256 + 4 * 32 * 4 * (128 + 32) * 4
     dec = L.bi_attention_decode
     args = [A16, 4096, A16, A16, 100, A16, 64, A16, A16, 4096, 4, 32, 8, 128, 1000, 0.088, A16, ws, None]
     bad = list(args); bad[17] = ws - 4
@@ -134,6 +136,12 @@ def test_attention_validation(L):
     assert dec(*bad) == 1                                     # max_kv_len > capacity
     bad = list(args); bad[10] = 0
     assert dec(*bad) == 0                                     # S == 0
+    bad = list(args); bad[11] = 512; bad[12] = 512; bad[1] = bad[9] = 512 * 128
+    assert dec(*bad) == 2                                     # Hkv > 256
+    # (split, KV head) work items beyond 2^30: refused before any device call
+    huge = list(args); huge[10] = 2048; huge[11] = 256; huge[12] = 256; huge[1] = huge[9] = 256 * 128
+    huge[6] = 1 << 16; huge[14] = 1 << 20; huge[17] = L.bi_attention_workspace_bytes(2048, 256, 128, 1 << 20)
+    assert dec(*huge) == 2
     pre = L.bi_attention_prefill
     pargs = [A16, 4096, A16, A16, A16, A16, 100, A16, 64, A16, 4096, 2, 300, 32, 8, 128, 200, 0.088, None]
     bad = list(pargs); bad[14] = 3
@@ -161,10 +169,13 @@ def test_attention_decode_noalloc_validation(L):
     assert f(*bad) == 1                                       # null q
     bad = list(args); bad[10] = 0
     assert f(*bad) == 0                                       # S == 0: no-op
-    # the limit: S * Hq * ceil(max_kv_len / 256) partials of 130 floats <= 64 MiB
+    # the limit: the work counter (with alignment slack) and S * Hq *
+    # ceil(max_kv_len / 256) rows of 128 + 32 floats in 64 MiB
     assert ops.NOALLOC_SCRATCH_BYTES == 64 << 20
-    limit_splits = ops.NOALLOC_SCRATCH_BYTES // (130 * 4)
-    assert limit_splits == 129055
+    limit_splits = (ops.NOALLOC_SCRATCH_BYTES - 511) // (160 * 4)
+    assert limit_splits == 104856
+    assert L.bi_attention_workspace_bytes(1, 1, 128, 256 * limit_splits) <= ops.NOALLOC_SCRATCH_BYTES
+    assert L.bi_attention_workspace_bytes(1, 1, 128, 256 * (limit_splits + 1)) > ops.NOALLOC_SCRATCH_BYTES
     big = list(args); big[10] = 256; big[14] = 32768          # 256 * 32 * 128 splits
     assert L.bi_attention_workspace_bytes(256, 32, 128, 32768) > ops.NOALLOC_SCRATCH_BYTES
     assert f(*big) == 3                                       # BI_ERR_WORKSPACE_TOO_SMALL

@@ -50,7 +50,7 @@ def _both(ops, lens, cache, table, q_bits, max_len):
 
 
 def test_noalloc_decode_equals_workspace_decode_on_two_calls(ops):
-    # first call: 48 sequences up to 8192 tokens (48 * 32 * 32 split partials, 25.6 MB of scratch)
+    # first call: 48 sequences up to 8192 tokens (48 * 32 * 32 split partials, 31.5 MB of scratch)
     lens, cache, table, q = _case(71, 48, 8192)
     log(f"noalloc call 1: S=48 max_len=8192 ws={ops.bi_attention_workspace_bytes(48, 32, 128, 8192)}")
     ref, out = _both(ops, lens, cache, table, q, 8192)
@@ -60,10 +60,11 @@ def test_noalloc_decode_equals_workspace_decode_on_two_calls(ops):
     log("noalloc call 2: S=5 max_len=600 Hq=16 Hkv=4")
     ref2, out2 = _both(ops, lens2, cache2, table2, q2, 600)
     assert np.array_equal(out2, ref2)
-    # the largest call the scratch holds: S * Hq * splits = 126 * 32 * 32 = 129024 <= 129055
-    lens3, cache3, table3, q3 = _case(73, 126, 8192)
-    assert ops.bi_attention_workspace_bytes(126, 32, 128, 8192) <= ops.NOALLOC_SCRATCH_BYTES
-    log("noalloc call 3: S=126 max_len=8192 (scratch nearly full)")
+    # the largest call the scratch holds: S * Hq * splits = 102 * 32 * 32 = 104448 <= 104856
+    lens3, cache3, table3, q3 = _case(73, 102, 8192)
+    assert ops.bi_attention_workspace_bytes(102, 32, 128, 8192) <= ops.NOALLOC_SCRATCH_BYTES
+    assert ops.bi_attention_workspace_bytes(103, 32, 128, 8192) > ops.NOALLOC_SCRATCH_BYTES
+    log("noalloc call 3: S=102 max_len=8192 (scratch nearly full)")
     ref3, out3 = _both(ops, lens3, cache3, table3, q3, 8192)
     assert np.array_equal(out3, ref3)
 
