@@ -18,12 +18,17 @@
 //          32c + 8(i>>2) + 4h + (i&3) in MFMA row i, so that afterwards lane
 //          (col = q, grp) holds tokens 32c + 8 grp + j, j = 0..7, in registers
 //          (tile 0 rows -> j = 0..3, tile 1 rows -> j = 4..7).  Each tile is an
-//          MFMA chain over the 4 head-dim chunks of 32 in ascending order from 0.
-//          s = acc * (scale * log2 e), fp32.  Masked tokens get -inf.
-//  max     m = max over the split's valid tokens (exact, order-free).
-//  weights p = exp2(s - m) (v_exp_f32), rounded to bf16; masked -> 0.
-//  sum     l: each lane adds its bf16 weights as fp32 for c = 0..7, j = 0..7 in
-//          that order, then lanes combine with xor-16 then xor-32 shuffles.
+//          MFMA chain over the 4 head-dim chunks of 32 in ascending order from 0:
+//          the raw score a (fp32).  Masked tokens get a = -inf.  With
+//          c = |scale| * log2 e (fp32; for a negative scale the query is
+//          negated, which negates every product and sum exactly):
+//  max     m = fl(max over the split's valid tokens of a  *  c) (the max is
+//          exact and order-free; -inf when no token is valid).
+//  weights p = exp2(fma(a, c, -m)) (one rounding, v_exp_f32), rounded to bf16;
+//          masked -> 0.
+//  sum     l = the MFMA chain ones^T P^T over chunks c = 0..7 in ascending
+//          order from 0 (the values' chain shape with an all-ones A operand),
+//          so the weights are summed exactly as the values weight them.
 //  values  O^T = V^T P^T, 8 head-dim tiles of 16; each an MFMA chain over the
 //          chunks c = 0..7 in ascending order from 0, the B operand being the
 //          lane's 8 bf16 weights (k-slot j <-> token 32c + 8 grp + j).
@@ -59,13 +64,31 @@ __device__ __forceinline__ f32x4 score_tile(const bf16x8 kf[4], const bf16x8 qf[
     return acc;
 }
 
-__device__ __forceinline__ float scaled_score(float acc, float scale_log2) { return acc * scale_log2; }
-
-// Weight of one token before rounding, given the split max of its row.
-__device__ __forceinline__ float weight_f32(float s, float m, bool valid)
+// The split's max m from the max of its raw scores (c = |scale| log2 e > 0,
+// or 0 for a zero scale: a row with no valid token keeps m = -inf).
+__device__ __forceinline__ float split_max(float raw_max, float c)
 {
-    return valid ? hw_exp2(s - m) : 0.0f;
+    return raw_max == -INFINITY ? -INFINITY : raw_max * c;
 }
+
+// Weight of one token before rounding: exp2(fma(a, c, -m)).  In a split with
+// masked tokens (a = -inf) the masked form returns 0 for them.
+__device__ __forceinline__ float weight_of(float a, float c, float m)
+{
+    return hw_exp2(__builtin_fmaf(a, c, -m));
+}
+__device__ __forceinline__ float weight_of_masked(float a, float c, float m)
+{
+    return a == -INFINITY ? 0.0f : weight_of(a, c, m);
+}
+
+// Queries enter with their sign flipped when the scale is negative, and the
+// kernels use c = |scale log2 e|.
+__device__ __forceinline__ u32x4 q_for_scale(u32x4 q, float scale_log2)
+{
+    return scale_log2 < 0.0f ? (q ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}) : q;
+}
+__device__ __forceinline__ float c_of_scale(float scale_log2) { return scale_log2 < 0.0f ? -scale_log2 : scale_log2; }
 
 // Round 8 weights (j = 0..7) to bf16 and pack them into one MFMA operand.
 __device__ __forceinline__ bf16x8 pack_weights(const float p[8])
@@ -78,25 +101,13 @@ __device__ __forceinline__ bf16x8 pack_weights(const float p[8])
     return as_bf16x8(v);
 }
 
-// Running sum of the weights: add the 8 bf16 weights of one chunk, j ascending.
-__device__ __forceinline__ float lsum_add(float acc, bf16x8 p)
+// One step of the weight-sum chain: l tile += ones^T(chunk) * P^T(chunk).
+// Every entry of the lane's accumulator ends up holding l of its column.
+__device__ __forceinline__ bf16x8 ones_bf16x8()
 {
-    const u32x4 v = as_u32x4(p);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        acc = acc + bf16_to_f32(v[e] & 0xffffu);
-        acc = acc + bf16_to_f32(v[e] >> 16);
-    }
-    return acc;
+    return as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 }
-
-// Combine the four lane groups (grp 0..3) of one column: xor 16 then xor 32.
-__device__ __forceinline__ float lsum_finish(float acc)
-{
-    acc = acc + __shfl_xor(acc, 16, 64);
-    acc = acc + __shfl_xor(acc, 32, 64);
-    return acc;
-}
+__device__ __forceinline__ f32x4 lsum_step(bf16x8 pf, f32x4 acc) { return mfma16(ones_bf16x8(), pf, acc); }
 
 // Max across the four lane groups of one column (exact).
 __device__ __forceinline__ float colmax_finish(float v)

@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
         if (tid == 0) s_ticket = 2 * P + (int)drawn;
         bf16x8 qf[4];
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) qf[dc] = as_bf16x8(qok ? qraw[dc] : zero_u32x4());
+        for (int dc = 0; dc < 4; ++dc) qf[dc] = as_bf16x8(q_for_scale(qok ? qraw[dc] : zero_u32x4(), scale_log2));
 
         // block of tokens 32 c + 8 grp .. + 7 for the two chunks c = 2 wave + cc
         // this wave scores (a lane read across the wave, no LDS round trip)
@@ -387,12 +387,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
                 for (int r = 0; r < 4; ++r) {
                     const int j = 4 * h + r;
                     const bool valid = whole || (blk_ok[cc] && (t0 + 32 * c + 8 * grp + j) < L);
-                    sv[cc][j] = valid ? scaled_score(acc[r], scale_log2) : -INFINITY;
+                    sv[cc][j] = valid ? acc[r] : -INFINITY;
                 }
             }
         }
 
-        // split max across the four waves
+        // split max across the four waves (of the raw scores; scaled once)
         float mx = -INFINITY;
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
@@ -401,7 +401,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
         mx = colmax_finish(mx);
         if (grp == 0) s_max[wave][col] = mx;
         lds_barrier();
-        const float m = fmaxf(fmaxf(s_max[0][col], s_max[1][col]), fmaxf(s_max[2][col], s_max[3][col]));
+        const float c_scale = c_of_scale(scale_log2);
+        const float m = split_max(fmaxf(fmaxf(s_max[0][col], s_max[1][col]), fmaxf(s_max[2][col], s_max[3][col])),
+                                  c_scale);
         const int t_after = s_ticket;
         int s2, i2, g2;
         ticket_item(t_after, s2, i2, g2);
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
             float wv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                wv[j] = weight_f32(sv[cc][j], m, whole || (blk_ok[cc] && (t0 + 32 * c + 8 * grp + j) < L));
+                wv[j] = whole ? weight_of(sv[cc][j], c_scale, m) : weight_of_masked(sv[cc][j], c_scale, m);
             st16(&s_pt[col * kPtStride + 32 * c + 8 * grp], as_u32x4(pack_weights(wv)));
         }
         lds_barrier();
@@ -441,15 +443,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
         f32x4 o[2];
         o[0] = f32x4{0.f, 0.f, 0.f, 0.f};
         o[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float ls = 0.0f;
+        f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
             const bf16x8 pf = as_bf16x8(ld16(&s_pt[col * kPtStride + 32 * c + 8 * grp]));
-            ls = lsum_add(ls, pf);
+            lacc = lsum_step(pf, lacc);
 #pragma unroll
             for (int dd = 0; dd < 2; ++dd) o[dd] = pv_step(as_bf16x8(vv[c][dd]), pf, o[dd]);
         }
-        ls = lsum_finish(ls);
+        const float ls = lacc[0];
 
         store_prepare(o, ls, m, s, i, g, t0 == 0 && Lseq <= split_len, st_v, st_p);
         lds_barrier();     // s_max / s_pt are reused by the next item

@@ -100,10 +100,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const int wave_pos0 = p0 + tq0;                  // the smallest position among them
     const int nsplit = (p0 + last) / kSplit + 1;
 
+    const float c_scale = c_of_scale(scale_log2);
     bf16x8 qf[4];
     const uint16_t* qrow = q + (int64_t)(qs + tq) * ldq + (int64_t)h * kD + 8 * grp;
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) qf[dc] = as_bf16x8(cvalid ? ld16(qrow + 32 * dc) : zero_u32x4());
+    for (int dc = 0; dc < 4; ++dc)
+        qf[dc] = as_bf16x8(q_for_scale(cvalid ? ld16(qrow + 32 * dc) : zero_u32x4(), scale_log2));
 
     // block ids of every cache block this workgroup reads, once (-1: none / invalid)
     const int nblk_used = min((L + kBlock - 1) / kBlock, nsplit * (kSplit / kBlock));
@@ -168,11 +170,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         // wavefront sees the whole split (all but the diagonal splits) the
         // causal mask is dropped: same values, fewer instructions.
         bf16x8 pf[kChunks];
-        float mx = -INFINITY, ls = 0.0f;
+        float mx = -INFINITY;
+        f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
         auto softmax_part = [&](auto masked) {
             constexpr bool kMasked = decltype(masked)::value;
             float sv[kChunks][8];
-            bf16x8 kf[2][4];             // [step parity][dc]: the next tile's K operands load while this one multiplies
+            // [step mod 3][dc]: the K operands of the next two tiles load while
+            // this one multiplies
+            bf16x8 kf[3][4];
             auto load_k = [&](int st, bf16x8 (&dst)[4]) __attribute__((always_inline)) {
                 const int row = 32 * (st >> 1) + score_row_token(col, st & 1);
 #pragma unroll
@@ -180,46 +185,39 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
                     dst[dc] = *reinterpret_cast<const bf16x8*>(s_k + row * kD + (((4 * dc + grp) ^ kswz(row)) * 8));
             };
             load_k(0, kf[0]);
+            load_k(1, kf[1]);
+            float raw_max = -INFINITY;
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
 #pragma unroll
                 for (int th = 0; th < 2; ++th) {
                     const int st = 2 * c + th;
-                    if (st + 1 < 2 * kChunks) load_k(st + 1, kf[(st + 1) & 1]);
+                    if (st + 2 < 2 * kChunks) load_k(st + 2, kf[(st + 2) % 3]);
                     // only VALU / SALU work may be scheduled across: the loads stay ahead
                     __builtin_amdgcn_sched_barrier(0x6);
-                    const f32x4 acc = score_tile(kf[st & 1], qf);
+                    const f32x4 acc = score_tile(kf[st % 3], qf);
                     bool blk_ok = true;
                     if constexpr (kMasked) blk_ok = !bad || s_bt[(t0 >> 4) + 2 * c + (grp >> 1)] >= 0;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = 4 * th + r;
-                        if constexpr (kMasked) {
-                            const bool valid = blk_ok && (t0 + 32 * c + 8 * grp + j) <= pos;
-                            sv[c][j] = valid ? scaled_score(acc[r], scale_log2) : -INFINITY;
-                        } else {
-                            sv[c][j] = scaled_score(acc[r], scale_log2);
-                        }
+                        float a = acc[r];
+                        if constexpr (kMasked) a = blk_ok && (t0 + 32 * c + 8 * grp + j) <= pos ? a : -INFINITY;
+                        sv[c][j] = a;
+                        raw_max = fmaxf(raw_max, a);
                     }
                 }
             }
-#pragma unroll
-            for (int c = 0; c < kChunks; ++c)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) mx = fmaxf(mx, sv[c][j]);
-            mx = colmax_finish(mx);
+            mx = split_max(colmax_finish(raw_max), c_scale);
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
-                bool blk_ok = true;
-                if constexpr (kMasked) blk_ok = !bad || s_bt[(t0 >> 4) + 2 * c + (grp >> 1)] >= 0;
                 float wv[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    wv[j] = weight_f32(sv[c][j], mx, kMasked ? blk_ok && (t0 + 32 * c + 8 * grp + j) <= pos : true);
+                    wv[j] = kMasked ? weight_of_masked(sv[c][j], c_scale, mx) : weight_of(sv[c][j], c_scale, mx);
                 pf[c] = pack_weights(wv);
-                ls = lsum_add(ls, pf[c]);
+                lacc = lsum_step(pf[c], lacc);
             }
-            ls = lsum_finish(ls);
         };
         if (wave_full && t0 + kSplit - 1 <= wave_pos0 && !bad)
             softmax_part(std::false_type{});
@@ -236,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto values_part = [&](auto tail) {
             constexpr bool kTail = decltype(tail)::value;
-            u32x4 vf[2][4];              // [step parity][dt % 4]: the next half chunk's V operands load while this one multiplies
+            u32x4 vf[3][4];              // [step mod 3][dt % 4]: the V operands of the next two half chunks load while this one multiplies
             auto load_v = [&](int st, u32x4 (&dst)[4]) __attribute__((always_inline)) {
                 const int b = 2 * (st >> 1) + (grp >> 1);
 #pragma unroll
@@ -244,6 +242,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
                     dst[k] = ld16(s_v + b * (kD * kBlock) + (16 * (4 * (st & 1) + k) + col) * kBlock + (grp & 1) * 8);
             };
             load_v(0, vf[0]);
+            load_v(1, vf[1]);
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
                 const int tok = t0 + 32 * c + 8 * grp;
@@ -251,10 +250,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
                 for (int dt = 0; dt < 8; ++dt) {
                     const int st = 2 * c + (dt >> 2);
                     if ((dt & 3) == 0) {
-                        if (st + 1 < 2 * kChunks) load_v(st + 1, vf[(st + 1) & 1]);
+                        if (st + 2 < 2 * kChunks) load_v(st + 2, vf[(st + 2) % 3]);
                         __builtin_amdgcn_sched_barrier(0x6);
                     }
-                    u32x4 v = vf[st & 1][dt & 3];
+                    u32x4 v = vf[st % 3][dt & 3];
                     if constexpr (kTail) {
                         if (tok + 8 > L) v = tok >= L ? zero_u32x4() : keep_first(v, L - tok);
                         if (bad && tok < L && s_bt[tok >> 4] < 0) v = zero_u32x4();
@@ -268,6 +267,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         else
             values_part(std::true_type{});
         // ---------------- fold
+        const float ls = lacc[0];
         if (i == 0) {
             M = mx;
             Lam = ls;

@@ -254,3 +254,26 @@ def test_invalid_block_ids_are_masked_in_decode_and_prefill(ops, orc):
     for p in (0, 300, 319, 320, 335, 336, 511, 512, 600, 767, 768, 880, 890, 999):
         dp = decode(ops, cache, table, q[p][None], np.array([p + 1], np.int32), max_len=L)
         assert np.array_equal(dp[0], pre[p]), f"decode vs prefill p={p}"
+
+
+@pytest.mark.parametrize("scale", [-1.0 / math.sqrt(128), 0.0, 4.0 / math.sqrt(128)])
+def test_scale_sign_and_zero(ops, orc, scale):
+    """Any scale: a negative one enters as negated queries with |scale| (exact),
+    a zero one gives uniform weights.  Parity with the oracle at that scale, and
+    decode at length p + 1 equals prefill row p bit for bit."""
+    log(f"scale {scale}")
+    g = np.random.default_rng(91)
+    P0, T = 500, 200
+    L = P0 + T
+    k, v = I.kv_sequence(I.TAG_PREFILL, 9, 0, L)
+    cache, table = make_cache(g, [(k, v)])
+    q = I.queries(I.TAG_PREFILL, 9, T)
+    out = host_bits(ops.bi_attention_prefill(dev_bf16(q), dev_i32(np.array([0, T], np.int32)),
+                                             dev_i32(np.array([L], np.int32)), cache.k, cache.v,
+                                             dev_i32(table), T, scale))
+    o16, o64 = orc.attention(q, np.arange(P0, L), k, v, scale)
+    check_bf16(out, o64, f"prefill scale={scale}", axis=-1)
+    for r in (0, 99, 199):
+        d = host_bits(ops.bi_attention_decode(dev_bf16(q[r][None]), cache.k, cache.v, dev_i32(table),
+                                              dev_i32(np.array([P0 + r + 1], np.int32)), L, scale))
+        assert np.array_equal(d[0], out[r]), f"decode vs prefill row {r} scale={scale}"
