@@ -375,7 +375,7 @@ def main():
             "workload": "llama8b-projection sweep (RMSNorm 4096 + bf16 GEMM 4096->4096 and 4096->14336, "
                         "M=1..64,128,256,512,1024,2048) + paged decode S=256 + causal prefill 8192",
             "M_sweep": list(I.M_SWEEP), "hidden": H, "N": list(Ns),
-            "gemm_tile": "128x64x128 workgroup tile, 8 waves of 32x32 (2x2 MFMA tiles), v_mfma_f32_16x16x32_bf16, 3-stage global_load_lds pipeline, next k tile read from LDS during the current MFMAs",
+            "gemm_tile": "one per-element chain (fp32 from 0, one v_mfma_f32_16x16x32_bf16 per 32-wide k chunk, ascending) dealt out by four tiles chosen by shape, all bitwise equal: 64x32x128 for M<=32, else the largest of 64x64x128 / 128x64x128 / 128x128x64 no taller than M rounded up to 64 giving >= 3/4 of the CUs in workgroups; 3-stage global_load_lds pipeline, next k tile read from LDS during the current MFMAs",
             "value_basis": "GEMM flops of the sweep / GPU time of the projection phase (HIP graph replay)",
             "graph_matches_eager": graph_matches_eager,
             "gpu_sclk_mhz_after_timed_steps": sclk_after,

@@ -1,5 +1,5 @@
-// gemm.hip -- batch-invariant dense matmul: ONE MFMA tile configuration for
-// every shape.
+// gemm.hip -- batch-invariant dense matmul: ONE reduction chain per output
+// element for every shape.
 //
 // Table row 行列乗算（MatMul） of the post "論文／ブログ「Defeating Nondeterminism
 // in LLM Inference」の技術的なポイント" (mobiles-han.blogspot.com), section
@@ -7,41 +7,88 @@
 // "元OpenAIの研究者ら、AIの応答が毎回違う理由をついに解明", section
 // 解決へのアプローチ: libraries pick split-K or drop the matrix units for some
 // sizes, which changes each output's reduction order with the batch; the fix
-// is one kernel configuration, decided in advance, for all shapes.
+// is a kernel whose reduction order is decided in advance for all shapes.
 //
 // Reduction order of an output c[m][n] (the only thing batch invariance needs
 // fixed): an fp32 accumulator starts at 0; one v_mfma_f32_16x16x32_bf16 per
 // 32-wide k chunk, chunks in ascending k; inside a chunk, lane group g always
-// supplies k = 8g..8g+7.  An MFMA result element depends only on its own row
+// supplies k = 8g..8g+7; the bias (addmm) is added once to the fp32 sum, then
+// the result is rounded.  An MFMA result element depends only on its own row
 // and column operands, so nothing in the chain depends on M, N, the tile's
-// place in the grid or the row's place in the tile.  No split-K, no stream-K,
-// no shape-dependent dispatch.
+// size, its place in the grid or the row's place in the tile.  No split-K, no
+// stream-K, no other instruction or k order for any shape.
 //
-// The one configuration (BiTile in gemm_kernel.hpp), chosen by timing the
-// whole M = 1..2048 sweep of Llama-8B projections (N = 4096 and 14336,
-// K = 4096) on MI355X against a dozen tiles with the same chain:
-//   * workgroup tile 128 (m) x 64 (n) x 128 (k), 512 threads = 8 wavefronts
-//     in a 4 (m) x 2 (n) arrangement, each wavefront a 32 x 32 tile of four
-//     16 x 16 MFMA tiles that share their operand reads (one 16-byte LDS read
-//     per MFMA).  Large M is bound by what the L2 delivers into the CUs'
-//     LDS, so the tile's flops per byte loaded (2 BM BN / (2 (BM + BN)) =
-//     43 flop/B) set its speed; small M streams W, and 64-wide n tiles still
-//     give N = 4096 sixty-four workgroups to stream it with;
-//   * operands go global -> LDS with global_load_lds_dwordx4, three 48 KB
-//     stages (144 KB, one workgroup per CU);
+// What the shape does choose is how the outputs are dealt to workgroups: four
+// tiles of the one kernel template (gemm_kernel.hpp), all with that chain --
+// 64 x 32 x 128, 64 x 64 x 128, 128 x 64 x 128 and 128 x 128 x 64 (m x n x k).
+// Their results are identical bit for bit (checked for every M of the
+// Llama-8B sweep against rows computed inside a 2048-row batch, by the GPU
+// tests), so the choice changes speed only.  Rule, from timing all four at
+// every M = 1..64, 128, ..., 2048 of the sweep (N = 4096 and 14336, K = 4096)
+// on MI355X: for M <= 32 the 64 x 32 tile (the most workgroups to stream the
+// weights); otherwise the largest tile, no taller than M rounded up to 64,
+// that still gives at least three quarters of the CU count in workgroups.
+// It picks the fastest of the four at every point measured (sweep 260 TFLOP/s
+// against 201 for the 128 x 64 x 128 tile alone; 2048 x 14336 at 0.30 of the
+// bf16 MFMA peak).  Common to all tiles:
+//   * wavefront tiles of 16 x 16 MFMA tiles that share their operand reads;
+//   * operands go global -> LDS with global_load_lds_dwordx4 through three
+//     stages;
 //   * the operands of k tile kt+1 are read from LDS while the MFMAs of k tile
 //     kt run (two register sets), so the LDS latency is off the critical path;
 //   * a tile wholly inside M, N and a whole number of k tiles runs a loop with
 //     no guards and fixed wait counts; edge tiles run the same chain with
 //     wave-uniform guards (rows out of range are neither loaded nor stored,
 //     and MFMAs of 16-row groups entirely past M are skipped);
-//   * LDS rows are 256 B with the 16-byte chunks XOR-swizzled by (row & 15):
-//     the 16 rows of an MFMA operand read hit distinct 16-byte slots, no bank
-//     conflicts on gfx950;
+//   * 16-byte LDS chunks XOR-swizzled by row: the 16 rows of an MFMA operand
+//     read hit distinct 16-byte slots, no bank conflicts on gfx950;
 //   * tiles are dealt to the 8 XCDs in contiguous ranges of a grouped order
 //     (bands of 4 m tiles, n-major inside a band).
-// No split-K, no stream-K, no shape-dependent choice of tile, MFMA or k order.
+#include <mutex>
+
 #include "gemm_kernel.hpp"
+
+namespace {
+
+using TileS = GemmTile<64, 32, 128, 4, 2, 3>;
+using TileQ = GemmTile<64, 64, 128, 2, 2, 3>;
+using TileM = BiTile;                                // 128 x 64 x 128
+using TileL = GemmTile<128, 128, 64, 2, 4, 3>;
+
+int device_cus()
+{
+    static std::mutex mu;
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] <= 0) {
+        int n = 0;
+        cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+    }
+    return cus[dev];
+}
+
+int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const void* bias, void* c,
+                  int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, void* stream)
+{
+    int pick = 0;                                    // 0 S, 1 Q, 2 M, 3 L
+    if (M > 32) {
+        const int64_t need = (int64_t)device_cus() * 3 / 4;
+        const int64_t cap = (M + 63) / 64 * 64;      // no tile taller than M rounded up to 64
+        const int64_t bm[4] = {64, 64, 128, 128}, bn[4] = {32, 64, 64, 128};
+        for (int t = 0; t < 4; ++t)
+            if (bm[t] <= cap && ((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]) >= need) pick = t;
+    }
+    switch (pick) {
+    case 1: return gemm_launch<TileQ>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 2: return gemm_launch<TileM>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 3: return gemm_launch<TileL>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    default: return gemm_launch<TileS>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    }
+}
+
+}  // namespace
 
 extern "C" int bi_matmul(const void* a, int64_t lda, const void* wt, int64_t ldw, void* c,
                          int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, void* stream)
@@ -49,11 +96,11 @@ extern "C" int bi_matmul(const void* a, int64_t lda, const void* wt, int64_t ldw
     BI_TRY_BEGIN
     const int v = gemm_validate(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K);
     if (v != BI_OK) return v < 0 ? BI_OK : v;
-    return gemm_launch<BiTile>(a, lda, wt, ldw, nullptr, c, ldc, c_dtype, M, N, K, stream);
+    return gemm_dispatch(a, lda, wt, ldw, nullptr, c, ldc, c_dtype, M, N, K, stream);
     BI_TRY_END
 }
 
-// addmm: the same kernel and K chain, the bias row added to the fp32 result
+// addmm: the same kernels and K chain, the bias row added to the fp32 result
 // once, before the output rounding.
 extern "C" int bi_addmm(const void* a, int64_t lda, const void* wt, int64_t ldw, const void* bias, void* c,
                         int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, void* stream)
@@ -62,6 +109,6 @@ extern "C" int bi_addmm(const void* a, int64_t lda, const void* wt, int64_t ldw,
     const int v = gemm_validate(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K);
     if (v != BI_OK) return v < 0 ? BI_OK : v;
     if (!bias || !bi_aligned(bias, 8)) return BI_ERR_INVALID_ARGUMENT;
-    return gemm_launch<BiTile>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    return gemm_dispatch(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     BI_TRY_END
 }

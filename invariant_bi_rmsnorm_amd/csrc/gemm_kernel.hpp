@@ -95,7 +95,8 @@ struct GemmTile {
     }
 };
 
-// The library's one configuration (see gemm.hip for why this one).
+// The 128 x 64 x 128 tile, one of the four the library deals outputs with
+// (gemm.hip); every tile computes each output with the same chain.
 using BiTile = GemmTile<128, 64, 128, 4, 2, 3>;
 constexpr int kGemmGroup = 4;          // m tiles per band of the tile order
 

@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import re
 import glob
 import hashlib
 import json
@@ -57,9 +58,10 @@ def _one(pattern, d):
 
 
 def short(name: str) -> str:
-    # the GEMM template: libbi.so's one tile vs the baseline library's tiles (tag 1)
+    # the GEMM template: libbi.so's tiles (tag 0) vs the baseline library's tiles (tag 1)
     if "gemm_kernel<" in name:
-        return "gemm_kernel" if "GemmTile<128, 64, 128, 4, 2, 3, 0>" in name else "gemm_kernel (baseline lib)"
+        m = re.search(r"GemmTile<\d+, \d+, \d+, \d+, \d+, \d+, (\d+)>", name)
+        return "gemm_kernel" if m and m.group(1) == "0" else "gemm_kernel (baseline lib)"
     for k in KERNELS:
         if name.startswith(k) or f" {k}" in name or name.startswith(f"(anonymous namespace)::{k}"):
             return k
