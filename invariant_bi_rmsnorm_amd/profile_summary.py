@@ -39,7 +39,7 @@ GEMM_N = (4096, 14336)
 M_SWEEP = list(range(1, 65)) + [128, 256, 512, 1024, 2048]
 
 KERNELS = ("gemm_kernel", "rmsnorm_kernel", "decode_split_kernel", "decode_combine_kernel",
-           "prefill_kernel", "kv_append_kernel", "copy_kernel")
+           "decode_ticket_reset", "prefill_kernel", "kv_append_kernel", "copy_kernel")
 
 
 def src_hash(*names):
@@ -82,7 +82,7 @@ def stats_md(d, out, cmd, title):
     total = sum(sum(v) for v in dur.values())
     lines = [f"# {title}", "", "Command (from the repository root, one MI355X):", "", "```", cmd, "```", "",
              "Kernel durations from rocprofv3's per-dispatch kernel trace (microseconds), per kernel "
-             "instantiation: `gemm_kernel` is libbi.so's one GEMM tile, `gemm_kernel (baseline lib)` the "
+             "instantiation: `gemm_kernel` is libbi.so's GEMM tiles, `gemm_kernel (baseline lib)` the "
              "non-invariant library's tiles.", "",
              "| kernel | calls | total us | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
     for k, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
