@@ -52,7 +52,8 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nvalid)
 // LDS layouts of one split.  K: [256 token rows][128 dims], 16-byte chunk ch of
 // row r at slot ch ^ kswz(r).  V^T: as in the cache, [16 blocks][128 dims][16
 // tokens], unswizzled.  Both operand reads are free of bank conflicts on gfx950
-// (SQ_LDS_BANK_CONFLICT reads zero for them); swapping the two 16-byte halves
+// (SQ_LDS_BANK_CONFLICT for the whole kernel is under 1 cycle per 100 LDS
+// instructions, so it cannot come from them); swapping the two 16-byte halves
 // of every other group of 8 V^T dim rows, as a 32-bank layout would want,
 // costs 4 conflict cycles per read here.
 __device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
