@@ -499,19 +499,45 @@ def main():
                                                                out=pout[:P]), 3)
                 fl = 4 * I.ATT_HQ * I.ATT_D * (P * (P + 1) // 2)
                 rows.append({"P": P, "us": round(us, 1), "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1)})
-            # the 8192-token prompt as four 2048-token chunks over the growing cache
-            CH = 2048
-            qs_ch = torch.tensor([0, CH], dtype=torch.int32, device=dev)
-            l_ch = [torch.tensor([(c + 1) * CH], dtype=torch.int32, device=dev) for c in range(P_PRE // CH)]
+            # the 8192-token prompt in chunks over the growing cache: 2048-token
+            # chunks (every chunk starts on a 256-token split boundary) and
+            # 2000-token chunks (they do not)
+            def chunk_calls(CH):
+                starts = list(range(0, P_PRE, CH))
+                args = []
+                for st in starts:
+                    n = min(CH, P_PRE - st)
+                    args.append((st, n, torch.tensor([0, n], dtype=torch.int32, device=dev),
+                                 torch.tensor([st + n], dtype=torch.int32, device=dev)))
 
-            def chunked():
-                for c in range(P_PRE // CH):
-                    ops.bi_attention_prefill(pq[c * CH:(c + 1) * CH], qs_ch, l_ch[c], pk, pv, ptbl, CH, scale,
-                                             out=pout[c * CH:(c + 1) * CH])
-            us = graph_us(chunked, 2)
-            rows.append({"P": P_PRE, "chunks": CH, "us": round(us, 1),
-                         "TFLOP/s": round(pre_flops / (us * 1e-6) / 1e12, 1)})
-            extra["prefill_P_sweep"] = rows
+                def run():
+                    for st, n, qs_c, l_c in args:
+                        ops.bi_attention_prefill(pq[st:st + n], qs_c, l_c, pk, pv, ptbl, n, scale,
+                                                 out=pout[st:st + n])
+                return run
+            for CH in (2048, 2000):
+                us = graph_us(chunk_calls(CH), 2)
+                rows.append({"P": P_PRE, "chunks": CH, "us": round(us, 1),
+                             "TFLOP/s": round(pre_flops / (us * 1e-6) / 1e12, 1)})
+            # the same calls through the non-invariant build, whose splits start
+            # at each chunk's first cache block instead of position 0
+            prev = ops.use_library(ops.NB_LIB_PATH)
+            try:
+                for r in rows:
+                    P = r["P"]
+                    if "chunks" in r:
+                        fn = chunk_calls(r["chunks"])
+                    else:
+                        qsP = torch.tensor([0, P], dtype=torch.int32, device=dev)
+                        lP = torch.tensor([P], dtype=torch.int32, device=dev)
+                        fn = (lambda P=P, qsP=qsP, lP=lP: ops.bi_attention_prefill(
+                            pq[:P], qsP, lP, pk, pv, ptbl, P, scale, out=pout[:P]))
+                    r["nb_us"] = round(graph_us(fn, 2 if "chunks" in r else 3), 1)
+            finally:
+                ops.use_library(prev)
+            extra["prefill_P_sweep"] = {"rows": rows,
+                                        "nb_us": "libbi_nb.so: splits start at each chunk's first cache "
+                                                 "block (not invariant under re-chunking)"}
         result["supplementary"] = extra
 
     # copy probe: a plain device copy of known size, the reference for what the
@@ -723,7 +749,7 @@ def main():
                 kh = kh.permute(0, 2, 1, 3).reshape(P_, I.ATT_HKV, I.ATT_D).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
                 vh = vh.permute(0, 3, 1, 2).reshape(P_, I.ATT_HKV, I.ATT_D).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
                 qp = pq[:P_].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-                gpu_row = [r for r in sup["prefill_P_sweep"] if r["P"] == P_ and "chunks" not in r][0]
+                gpu_row = [r for r in sup["prefill_P_sweep"]["rows"] if r["P"] == P_ and "chunks" not in r][0]
                 beside["prefill_P512"] = {"cpu_s": round(timed(lambda: oracle.attention(qp, np.arange(P_), kh, vh,
                                                                                          scale)), 3),
                                           "gpu_us": gpu_row["us"]}

@@ -15,10 +15,10 @@ BASELINE = os.path.join(CSRC, "baseline")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbi.so")
 # The non-invariant baseline library: the same ABI, with the batch-dependent
-# strategies of csrc/baseline/ in place of the invariant GEMM, RMSNorm and
-# decode.  Used only for measurement and to show the invariance tests can fail.
+# strategies of csrc/baseline/ in place of the invariant GEMM, RMSNorm,
+# decode and prefill.  Used only for measurement and to show the invariance tests can fail.
 LIB_NB = os.path.join(HERE, "libbi_nb.so")
-REPLACED_IN_NB = {"gemm.hip", "rmsnorm.hip", "attn_decode.hip"}
+REPLACED_IN_NB = {"gemm.hip", "rmsnorm.hip", "attn_decode.hip", "attn_prefill.hip"}
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

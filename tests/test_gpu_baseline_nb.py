@@ -1,5 +1,6 @@
 """The invariance tests have teeth: libbi_nb.so (same ABI, batch-dependent
-strategies for GEMM, RMSNorm and decode, as the pages describe ordinary
+strategies for GEMM, RMSNorm and decode and chunk-aligned prefill splits, as
+the pages describe ordinary
 kernels) computes correct results -- within the oracle tolerance and
 run-to-run deterministic -- whose bits nevertheless change with the batch, and
 the same tests that pass on libbi.so detect it.  The toy experiment on
@@ -81,6 +82,51 @@ def test_nb_decode_correct_but_batch_dependent(nb, orc):
     inb = host_bits(nb.bi_attention_decode(dev_bf16(q), c2.k, c2.v, dev_i32(t2), dev_i32(lens),
                                            int(lens.max()), SCALE))[5]
     assert not np.array_equal(alone, inb)
+
+
+def test_nb_prefill_correct_but_chunking_dependent(nb, orc):
+    """libbi_nb.so's prefill starts its splits at each chunk's first cache
+    block: a single-shot prompt, and chunks that start on multiples of 256,
+    give the library's bits; 1000-token chunks change them (the library keeps
+    them: test_prefill_chunked_equals_single_shot_and_decode), within the
+    oracle's tolerance and run-to-run stable."""
+    from invariant_bi_rmsnorm_amd import ops as o
+    g = np.random.default_rng(6)
+    P = 3001
+    k, v = I.kv_sequence(I.TAG_PREFILL, 6, 0, P)
+    q = I.queries(I.TAG_PREFILL, 6, P)
+    cache, table = make_cache(g, [(k, v)])
+    qd = dev_bf16(q)
+    tbl = dev_i32(table)
+
+    def run(sizes):
+        outs, start = [], 0
+        for c in sizes:
+            out = o.bi_attention_prefill(qd[start:start + c], dev_i32([0, c]), dev_i32([start + c]), cache.k,
+                                         cache.v, tbl, c, SCALE)
+            outs.append(host_bits(out))
+            start += c
+        assert start == P
+        return np.concatenate(outs)
+
+    prev = o.use_library(o.DEFAULT_LIB_PATH)
+    try:
+        inv_single = run([P])
+        inv_chunked = run([1000, 1000, 1001])
+    finally:
+        o.use_library(prev)
+    assert np.array_equal(inv_chunked, inv_single)
+    assert np.array_equal(run([P]), inv_single), "single shot: splits start at 0 in both builds"
+    assert np.array_equal(run([512, 1024, P - 1536]), inv_single), "chunks on split boundaries"
+    nb_chunked = run([1000, 1000, 1001])
+    assert np.array_equal(run([1000, 1000, 1001]), nb_chunked)            # run-to-run stable
+    assert np.array_equal(nb_chunked[:1000], inv_single[:1000])           # first chunk starts at 0
+    rows_diff = np.mean(np.any(nb_chunked[1000:] != inv_single[1000:], axis=(1, 2)))
+    log(f"nb prefill: {rows_diff:.1%} of the rows of chunks 2-3 differ from single shot")
+    assert rows_diff > 0.5
+    pos = np.r_[1000:1040, 2950:3001]
+    _, o64 = orc.attention(q[pos], pos, k, v, SCALE)
+    check_bf16(nb_chunked[pos], o64, "nb chunked prefill", axis=-1)
 
 
 def test_nb_toy_experiment_gives_several_completions(nb):
