@@ -18,28 +18,36 @@
 // size, its place in the grid or the row's place in the tile.  No split-K, no
 // stream-K, no other instruction or k order for any shape.
 //
-// What the shape does choose is how the outputs are dealt to workgroups: four
-// tiles of the one kernel template (gemm_kernel.hpp), all with that chain --
-// 64 x 32 x 128, 64 x 64 x 128, 128 x 64 x 128 and 128 x 128 x 64 (m x n x k).
+// What the shape does choose is how the outputs are dealt to workgroups: seven
+// tiles of the one kernel template (gemm_kernel.hpp), all with that chain.
 // Their results are identical bit for bit (checked for every M of the
-// Llama-8B sweep against rows computed inside a 2048-row batch, by the GPU
-// tests), so the choice changes speed only.  Rule, from timing all four at
-// every M = 1..64, 128, ..., 2048 of the sweep (N = 4096 and 14336, K = 4096)
-// on MI355X: for M <= 32 the 64 x 32 tile (the most workgroups to stream the
-// weights); otherwise the largest tile, no taller than M rounded up to 64,
-// that still gives at least three quarters of the CU count in workgroups.
-// It picks the fastest of the four at every point measured (sweep 260 TFLOP/s
-// against 201 for the 128 x 64 x 128 tile alone; 2048 x 14336 at 0.30 of the
-// bf16 MFMA peak).  Common to all tiles:
+// Llama-8B sweep against rows computed inside a 2048-row batch, and at edge
+// shapes, by the GPU tests), so the choice changes speed only.  Rule, from
+// timing the tiles at every M of the sweep (N = 4096 and 14336, K = 4096) on
+// MI355X:
+//   * M <= 64 is bound by streaming the weights.  When 64-wide n tiles still
+//     give three quarters of the CU count in workgroups, 64 x 64 x 128;
+//     otherwise 16-wide n tiles with deep k tiles and more stages, so that
+//     every CU gets a workgroup with many weight bytes in flight:
+//     16 x 16 x 256 (M <= 16), 32 x 16 x 256 (M <= 32), 64 x 16 x 128 with
+//     six stages (M <= 64).  (N = 4096, M <= 16: 8.2 us against 15.7 for the
+//     64 x 32 x 128 tile.)
+//   * M > 64: the largest of 64 x 32 x 128, 64 x 64 x 128, 128 x 64 x 128 and
+//     128 x 128 x 64 (m x n x k) no taller than M rounded up to 64 that still
+//     gives three quarters of the CU count in workgroups (2048 x 14336 at 0.30
+//     of the bf16 MFMA peak).
+// A tile that sticks out past M runs the unguarded loop with its extra rows
+// reading row M-1; their results are never stored.  Common to all tiles:
 //   * wavefront tiles of 16 x 16 MFMA tiles that share their operand reads;
 //   * operands go global -> LDS with global_load_lds_dwordx4 through three
-//     stages;
+//     to six stages;
 //   * the operands of k tile kt+1 are read from LDS while the MFMAs of k tile
 //     kt run (two register sets), so the LDS latency is off the critical path;
-//   * a tile wholly inside M, N and a whole number of k tiles runs a loop with
-//     no guards and fixed wait counts; edge tiles run the same chain with
-//     wave-uniform guards (rows out of range are neither loaded nor stored,
-//     and MFMAs of 16-row groups entirely past M are skipped);
+//   * a tile inside N and a whole number of k tiles runs a loop with no
+//     guards and fixed wait counts; edge tiles (columns past N, a k tail) run
+//     the same chain with wave-uniform guards (rows out of range are neither
+//     loaded nor stored, and MFMAs of 16-row groups entirely past M are
+//     skipped);
 //   * 16-byte LDS chunks XOR-swizzled by row: the 16 rows of an MFMA operand
 //     read hit distinct 16-byte slots, no bank conflicts on gfx950;
 //   * tiles are dealt to the 8 XCDs in contiguous ranges of a grouped order
@@ -54,6 +62,9 @@ using TileS = GemmTile<64, 32, 128, 4, 2, 3>;
 using TileQ = GemmTile<64, 64, 128, 2, 2, 3>;
 using TileM = BiTile;                                // 128 x 64 x 128
 using TileL = GemmTile<128, 128, 64, 2, 4, 3>;
+using TileN16 = GemmTile<16, 16, 256, 1, 1, 4>;      // narrow tiles for small M
+using TileN32 = GemmTile<32, 16, 256, 2, 1, 6>;
+using TileN64 = GemmTile<64, 16, 128, 4, 1, 6>;
 
 int device_cus()
 {
@@ -72,9 +83,11 @@ int device_cus()
 int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const void* bias, void* c,
                   int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, void* stream)
 {
-    int pick = 0;                                    // 0 S, 1 Q, 2 M, 3 L
-    if (M > 32) {
-        const int64_t need = (int64_t)device_cus() * 3 / 4;
+    const int64_t need = (int64_t)device_cus() * 3 / 4;
+    int pick = 0;                                    // 0 S, 1 Q, 2 M, 3 L, 4 N16, 5 N32, 6 N64
+    if (M <= 64) {
+        pick = (N + 63) / 64 >= need ? 1 : M <= 16 ? 4 : M <= 32 ? 5 : 6;
+    } else {
         const int64_t cap = (M + 63) / 64 * 64;      // no tile taller than M rounded up to 64
         const int64_t bm[4] = {64, 64, 128, 128}, bn[4] = {32, 64, 64, 128};
         for (int t = 0; t < 4; ++t)
@@ -84,6 +97,9 @@ int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const
     case 1: return gemm_launch<TileQ>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     case 2: return gemm_launch<TileM>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     case 3: return gemm_launch<TileL>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 4: return gemm_launch<TileN16>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 5: return gemm_launch<TileN32>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 6: return gemm_launch<TileN64>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     default: return gemm_launch<TileS>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     }
 }

@@ -27,20 +27,20 @@ __device__ __forceinline__ void gemm_wait_vm()
     __builtin_amdgcn_s_waitcnt(imm);
 }
 
-// the same with a run-time (wave-uniform) count, 0..32
+// the same with a run-time (wave-uniform) count, 0..63 (larger counts wait for 63)
 __device__ __forceinline__ void gemm_wait_vm_upto(int n)
 {
     switch (n) {
 #define GEMM_WAIT_CASE(i) case i: gemm_wait_vm<i>(); break;
-        GEMM_WAIT_CASE(0) GEMM_WAIT_CASE(1) GEMM_WAIT_CASE(2) GEMM_WAIT_CASE(3) GEMM_WAIT_CASE(4)
-        GEMM_WAIT_CASE(5) GEMM_WAIT_CASE(6) GEMM_WAIT_CASE(7) GEMM_WAIT_CASE(8) GEMM_WAIT_CASE(9)
-        GEMM_WAIT_CASE(10) GEMM_WAIT_CASE(11) GEMM_WAIT_CASE(12) GEMM_WAIT_CASE(13) GEMM_WAIT_CASE(14)
-        GEMM_WAIT_CASE(15) GEMM_WAIT_CASE(16) GEMM_WAIT_CASE(17) GEMM_WAIT_CASE(18) GEMM_WAIT_CASE(19)
-        GEMM_WAIT_CASE(20) GEMM_WAIT_CASE(21) GEMM_WAIT_CASE(22) GEMM_WAIT_CASE(23) GEMM_WAIT_CASE(24)
-        GEMM_WAIT_CASE(25) GEMM_WAIT_CASE(26) GEMM_WAIT_CASE(27) GEMM_WAIT_CASE(28) GEMM_WAIT_CASE(29)
-        GEMM_WAIT_CASE(30) GEMM_WAIT_CASE(31)
+#define GEMM_WAIT_CASE8(i) GEMM_WAIT_CASE(i) GEMM_WAIT_CASE(i + 1) GEMM_WAIT_CASE(i + 2) GEMM_WAIT_CASE(i + 3) \
+    GEMM_WAIT_CASE(i + 4) GEMM_WAIT_CASE(i + 5) GEMM_WAIT_CASE(i + 6) GEMM_WAIT_CASE(i + 7)
+        GEMM_WAIT_CASE8(0) GEMM_WAIT_CASE8(8) GEMM_WAIT_CASE8(16) GEMM_WAIT_CASE8(24)
+        GEMM_WAIT_CASE8(32) GEMM_WAIT_CASE8(40) GEMM_WAIT_CASE8(48)
+        GEMM_WAIT_CASE(56) GEMM_WAIT_CASE(57) GEMM_WAIT_CASE(58) GEMM_WAIT_CASE(59) GEMM_WAIT_CASE(60)
+        GEMM_WAIT_CASE(61) GEMM_WAIT_CASE(62)
+#undef GEMM_WAIT_CASE8
 #undef GEMM_WAIT_CASE
-        default: gemm_wait_vm<32>(); break;
+        default: gemm_wait_vm<63>(); break;
     }
 }
 
@@ -81,17 +81,18 @@ struct GemmTile {
     static constexpr int kTN = kWCols / 16;
     static constexpr int kKS = BK / 32;                 // 32-wide k chunks per k tile
     static constexpr int kLdsElems = STAGES * kStage;
-    static_assert(kChunks == 8 || kChunks == 16, "k tile of 64 or 128");
+    static_assert(kChunks == 8 || kChunks == 16 || kChunks == 32, "k tile of 64, 128 or 256");
     static_assert(kALoads % kWaves == 0 && kWLoads % kWaves == 0, "every wavefront issues the same loads");
     static_assert(kTM >= 1 && kTN >= 1 && kWRows % 16 == 0 && kWCols % 16 == 0, "wavefront tile");
     static_assert(STAGES >= 3, "one stage being read, at least one in flight, one being refilled");
+    static_assert((STAGES - 1) * kPer <= 63, "loads in flight per wavefront fit the vmcnt counter");
     static_assert(kLdsElems * 2 <= 160 * 1024, "LDS of one CU");
     // LDS slot of 16-byte chunk c of row r (an involution).  The 16 rows one
     // MFMA operand read touches land in 16 distinct 16-byte slots of a 256-byte
     // bank row, so the reads are free of bank conflicts on gfx950.
     __device__ static __forceinline__ int slot(int row, int c)
     {
-        return kChunks == 16 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7));
+        return kChunks >= 16 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7));
     }
 };
 
@@ -210,15 +211,17 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
     // left once every wavefront has read it (its LDS reads done + barrier).
     OpW fw0, fw1;
     OpA fa0, fa1;
-    if (m0 + BM <= M && n0 + BN <= N && K % BK == 0) {
-        // ---- tile wholly inside M, N and a whole number of k tiles: no guards
+    if (n0 + BN <= N && K % BK == 0) {
+        // ---- tile inside N and a whole number of k tiles: no guards.  Rows of
+        // the tile past M load row M-1 instead (in bounds; their results are
+        // computed and never stored, and no other output reads them)
         // per-lane element offsets from the tile's first row (fixed for the
         // whole k loop; k moves the wave-uniform base)
         uint32_t ga[T::kAPer], gw[T::kWPer];
 #pragma unroll
         for (int i = 0; i < T::kAPer; ++i) {
             const int row = (wave + T::kWaves * i) * T::kRowsPerLoad + lrow;
-            ga[i] = (uint32_t)(row * lda + T::slot(row, lch) * 8);
+            ga[i] = (uint32_t)(min(row, M - 1 - m0) * lda + T::slot(row, lch) * 8);
         }
 #pragma unroll
         for (int i = 0; i < T::kWPer; ++i) {
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
         if (kt < KT) step(kt, fw0, fa0, fw1, fa1);
         gemm_wait_vm<0>();                           // no load may still write this LDS at exit
     } else {
-        // ---- edge tile (rows past M, columns past N, a K tail): rows out of
+        // ---- edge tile (columns past N, a K tail): rows out of
         // range are neither loaded nor stored; the load count per stage then
         // depends on how many rows are in range (wave-uniform)
         auto issue = [&](int kt, int s) __attribute__((always_inline)) {

@@ -202,6 +202,27 @@ def test_matmul_llama_batch_invariance_sweep(ops, N):
     assert np.array_equal(c, full[perm])
 
 
+def test_matmul_tile_edges_equal_bits(ops, orc):
+    """Shapes that put the tiles on their edge paths (N not a multiple of the
+    tile width, K not a multiple of the k tile, M not a multiple of the tile
+    height): every row of a batch of M equals the same row computed inside a
+    600-row batch, which another tile computes; sampled rows match the oracle."""
+    g = np.random.default_rng(11)
+    for N, K in ((1000, 4128), (4100, 512), (14336, 4096)):
+        log(f"matmul tile edges N={N} K={K}")
+        x = I.normal_bf16(g, (600, K))
+        wt = I.normal_bf16(g, (N, K), 0, 0.02)
+        xd, wd = dev_bf16(x), dev_bf16(wt)
+        full = host_bits(ops.bi_matmul(xd, wd))
+        for M in (1, 7, 16, 17, 31, 32, 33, 50, 64, 65, 130):
+            c = host_bits(ops.bi_matmul(xd[:M], wd))
+            assert np.array_equal(c, full[:M]), f"N={N} K={K} M={M}"
+            c = host_bits(ops.bi_matmul(xd[600 - M:], wd))
+            assert np.array_equal(c, full[600 - M:]), f"N={N} K={K} last M={M}"
+        rows = [0, 16, 599]
+        check_bf16(full[rows], orc.matmul_f64(x[rows], wt), f"matmul edges N={N} K={K}")
+
+
 def test_matmul_repeat_bitwise(ops):
     g = np.random.default_rng(9)
     a = dev_bf16(I.normal_bf16(g, (333, 2048)))
