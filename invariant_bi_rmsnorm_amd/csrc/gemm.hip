@@ -26,11 +26,12 @@
 // timing the tiles at every M of the sweep (N = 4096 and 14336, K = 4096) on
 // MI355X:
 //   * M <= 64 is bound by streaming the weights.  When 64-wide n tiles still
-//     give three quarters of the CU count in workgroups, 64 x 64 x 128;
-//     otherwise 16-wide n tiles with deep k tiles and more stages, so that
-//     every CU gets a workgroup with many weight bytes in flight:
-//     16 x 16 x 256 (M <= 16), 32 x 16 x 256 (M <= 32), 64 x 16 x 128 with
-//     six stages (M <= 64).  (N = 4096, M <= 16: 8.2 us against 15.7 for the
+//     give three quarters of the CU count in workgroups, 64 x 64 x 128, with
+//     non-temporal weight loads when the weight matrix is 64 MiB or more
+//     (N = 14336: 22-26 us against 25-28); otherwise narrow n tiles with
+//     deep k tiles and more stages, so that many weight bytes are in flight
+//     per CU: 16 x 32 x 256 (M <= 32), 64 x 16 x 128 with six stages
+//     (M <= 64).  (N = 4096, M <= 16: 7.6-8.1 us against 15.7 for the
 //     64 x 32 x 128 tile.)
 //   * M > 64: the largest of 64 x 32 x 128, 64 x 64 x 128, 128 x 64 x 128 and
 //     128 x 128 x 64 (m x n x k) no taller than M rounded up to 64 that still
@@ -62,9 +63,14 @@ using TileS = GemmTile<64, 32, 128, 4, 2, 3>;
 using TileQ = GemmTile<64, 64, 128, 2, 2, 3>;
 using TileM = BiTile;                                // 128 x 64 x 128
 using TileL = GemmTile<128, 128, 64, 2, 4, 3>;
-using TileN16 = GemmTile<16, 16, 256, 1, 1, 4>;      // narrow tiles for small M
-using TileN32 = GemmTile<32, 16, 256, 2, 1, 6>;
+using TileQn = GemmTile<64, 64, 128, 2, 2, 3, 0, 2>; // 64 x 64, weights read non-temporally
+using TileE = GemmTile<16, 32, 256, 1, 2, 4>;        // narrow tiles for small M
 using TileN64 = GemmTile<64, 16, 128, 4, 1, 6>;
+
+// a weight matrix at least this large is read once per call with M <= 64 and
+// is not worth keeping in the caches (a quarter of MI355X's 256 MB last-level
+// cache): its loads are non-temporal
+constexpr int64_t kStreamWeightBytes = 64ll << 20;
 
 int device_cus()
 {
@@ -84,9 +90,12 @@ int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const
                   int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, void* stream)
 {
     const int64_t need = (int64_t)device_cus() * 3 / 4;
-    int pick = 0;                                    // 0 S, 1 Q, 2 M, 3 L, 4 N16, 5 N32, 6 N64
+    int pick = 0;                                    // 0 S, 1 Q, 2 M, 3 L, 4 Qn, 5 E, 6 N64
     if (M <= 64) {
-        pick = (N + 63) / 64 >= need ? 1 : M <= 16 ? 4 : M <= 32 ? 5 : 6;
+        if ((N + 63) / 64 >= need)
+            pick = N * K * 2 >= kStreamWeightBytes ? 4 : 1;
+        else
+            pick = M <= 32 ? 5 : 6;
     } else {
         const int64_t cap = (M + 63) / 64 * 64;      // no tile taller than M rounded up to 64
         const int64_t bm[4] = {64, 64, 128, 128}, bn[4] = {32, 64, 64, 128};
@@ -97,8 +106,8 @@ int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const
     case 1: return gemm_launch<TileQ>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     case 2: return gemm_launch<TileM>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     case 3: return gemm_launch<TileL>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 4: return gemm_launch<TileN16>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 5: return gemm_launch<TileN32>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 4: return gemm_launch<TileQn>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 5: return gemm_launch<TileE>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     case 6: return gemm_launch<TileN64>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     default: return gemm_launch<TileS>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     }

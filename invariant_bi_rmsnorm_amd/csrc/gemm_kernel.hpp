@@ -52,17 +52,21 @@ __device__ __forceinline__ void gemm_wait_lds() { __builtin_amdgcn_s_waitcnt(0xc
 __device__ __forceinline__ void gemm_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // one wavefront-wide 1 KB load: 16 bytes per lane, global -> LDS (the LDS
-// destination is the wave's base address; lane l lands at byte 16 l)
+// destination is the wave's base address; lane l lands at byte 16 l); kPol is
+// the cache policy (0 default, 2 non-temporal)
+template <int kPol = 0>
 __device__ __forceinline__ void gemm_load_lds16(const uint16_t* g, uint16_t* l)
 {
-    __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, l, 16, 0, kPol);
 }
 
 // kLib tags which library instantiates the tile (0: libbi.so, 1: the baseline),
-// so profiles tell their kernels apart; it has no other effect.
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int kLib = 0>
+// so profiles tell their kernels apart; it has no other effect.  kWPol is the
+// cache policy of the weight loads.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int kLib = 0, int WPOL = 0>
 struct GemmTile {
     static constexpr int kBM = BM, kBN = BN, kBK = BK, kWM = WM, kWN = WN, kStages = STAGES;
+    static constexpr int kWPol = WPOL;
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kChunks = BK / 8;              // 16-byte chunks per row of a k tile
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
                 gemm_load_lds16(ak + ga[i], sa + (wave + T::kWaves * i) * 512);
 #pragma unroll
             for (int i = 0; i < T::kWPer; ++i)
-                gemm_load_lds16(wk + gw[i], sw + (wave + T::kWaves * i) * 512);
+                gemm_load_lds16<T::kWPol>(wk + gw[i], sw + (wave + T::kWaves * i) * 512);
         };
         // Every step issues one stage: past the last k tile it loads the last k
         // tile again into the slot just freed (never read again), so every
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(
                     const int row = inst * T::kRowsPerLoad + lrow;
                     const int gch = T::slot(row, lch);
                     if (n0 + row < N && kbase + gch * 8 < K)
-                        gemm_load_lds16(wt + (int64_t)(n0 + row) * ldw + kbase + gch * 8, sw + inst * 512);
+                        gemm_load_lds16<T::kWPol>(wt + (int64_t)(n0 + row) * ldw + kbase + gch * 8, sw + inst * 512);
                 }
             }
         };

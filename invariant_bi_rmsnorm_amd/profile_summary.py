@@ -60,7 +60,7 @@ def _one(pattern, d):
 def short(name: str) -> str:
     # the GEMM template: libbi.so's tiles (tag 0) vs the baseline library's tiles (tag 1)
     if "gemm_kernel<" in name:
-        m = re.search(r"GemmTile<\d+, \d+, \d+, \d+, \d+, \d+, (\d+)>", name)
+        m = re.search(r"GemmTile<\d+, \d+, \d+, \d+, \d+, \d+, (\d+)(?:, \d+)?>", name)
         return "gemm_kernel" if m and m.group(1) == "0" else "gemm_kernel (baseline lib)"
     for k in KERNELS:
         if name.startswith(k) or f" {k}" in name or name.startswith(f"(anonymous namespace)::{k}"):
