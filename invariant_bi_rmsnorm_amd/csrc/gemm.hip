@@ -18,7 +18,7 @@
 // size, its place in the grid or the row's place in the tile.  No split-K, no
 // stream-K, no other instruction or k order for any shape.
 //
-// What the shape does choose is how the outputs are dealt to workgroups: seven
+// What the shape does choose is how the outputs are dealt to workgroups: eight
 // tiles of the one kernel template (gemm_kernel.hpp), all with that chain.
 // Their results are identical bit for bit (checked for every M of the
 // Llama-8B sweep against rows computed inside a 2048-row batch, and at edge
@@ -33,10 +33,11 @@
 //     per CU: 16 x 32 x 256 (M <= 32), 64 x 16 x 128 with six stages
 //     (M <= 64).  (N = 4096, M <= 16: 7.6-8.1 us against 15.7 for the
 //     64 x 32 x 128 tile.)
-//   * M > 64: the largest of 64 x 32 x 128, 64 x 64 x 128, 128 x 64 x 128 and
-//     128 x 128 x 64 (m x n x k) no taller than M rounded up to 64 that still
-//     gives three quarters of the CU count in workgroups (2048 x 14336 at 0.30
-//     of the bf16 MFMA peak).
+//   * M > 64: the largest of 64 x 32 x 128, 64 x 64 x 128, 128 x 64 x 128,
+//     128 x 128 x 64 and 256 x 128 x 64 (m x n x k; the last with 64 x 64
+//     wavefront tiles, half the LDS reads per MFMA) no taller than M rounded
+//     up to 64 that still gives three quarters of the CU count in workgroups
+//     (512 x 14336: 66 us against 87 for 128 x 128 x 64).
 // A tile that sticks out past M runs the unguarded loop with its extra rows
 // reading row M-1; their results are never stored.  Common to all tiles:
 //   * wavefront tiles of 16 x 16 MFMA tiles that share their operand reads;
@@ -63,6 +64,7 @@ using TileS = GemmTile<64, 32, 128, 4, 2, 3>;
 using TileQ = GemmTile<64, 64, 128, 2, 2, 3>;
 using TileM = BiTile;                                // 128 x 64 x 128
 using TileL = GemmTile<128, 128, 64, 2, 4, 3>;
+using TileG = GemmTile<256, 128, 64, 4, 2, 3>;       // 8 wavefronts of 64 x 64
 using TileQn = GemmTile<64, 64, 128, 2, 2, 3, 0, 2>; // 64 x 64, weights read non-temporally
 using TileE = GemmTile<16, 32, 256, 1, 2, 4>;        // narrow tiles for small M
 using TileN64 = GemmTile<64, 16, 128, 4, 1, 6>;
@@ -90,7 +92,7 @@ int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const
                   int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, void* stream)
 {
     const int64_t need = (int64_t)device_cus() * 3 / 4;
-    int pick = 0;                                    // 0 S, 1 Q, 2 M, 3 L, 4 Qn, 5 E, 6 N64
+    int pick = 0;                                    // 0 S, 1 Q, 2 M, 3 L, 4 Qn, 5 E, 6 N64, 7 G
     if (M <= 64) {
         if ((N + 63) / 64 >= need)
             pick = N * K * 2 >= kStreamWeightBytes ? 4 : 1;
@@ -98,9 +100,10 @@ int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const
             pick = M <= 32 ? 5 : 6;
     } else {
         const int64_t cap = (M + 63) / 64 * 64;      // no tile taller than M rounded up to 64
-        const int64_t bm[4] = {64, 64, 128, 128}, bn[4] = {32, 64, 64, 128};
-        for (int t = 0; t < 4; ++t)
-            if (bm[t] <= cap && ((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]) >= need) pick = t;
+        const int64_t bm[5] = {64, 64, 128, 128, 256}, bn[5] = {32, 64, 64, 128, 128};
+        const int code[5] = {0, 1, 2, 3, 7};
+        for (int t = 0; t < 5; ++t)
+            if (bm[t] <= cap && ((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]) >= need) pick = code[t];
     }
     switch (pick) {
     case 1: return gemm_launch<TileQ>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
@@ -109,6 +112,7 @@ int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const
     case 4: return gemm_launch<TileQn>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     case 5: return gemm_launch<TileE>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     case 6: return gemm_launch<TileN64>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 7: return gemm_launch<TileG>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     default: return gemm_launch<TileS>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     }
 }
