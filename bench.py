@@ -577,7 +577,8 @@ def main():
             "invariant_TFLOP/s": round(gemm_flops_step / (inv_us * 1e-6) / 1e12, 3),
             "nb_TFLOP/s": round(gemm_flops_step / (nb_us * 1e-6) / 1e12, 3),
             "note": "the 138 GEMMs of the sweep as one HIP graph, invariant library vs libbi_nb.so "
-                    "(shape-tuned: split-K at M <= 64, a 128x128 tile where it fills the chip)"}
+                    "(the library's tiles and rule, plus split-K at M <= 64 where the 64x32 tiles fill at most half "
+                    "the CUs: N <= 4096)"}
     except Exception as e:  # context only
         result["baseline_nb_gemm_sweep"] = {"error": str(e)[:200]}
 

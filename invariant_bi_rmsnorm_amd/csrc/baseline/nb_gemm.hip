@@ -5,29 +5,23 @@
 // It does what the pages say ordinary libraries do (post 論文／ブログ「Defeating
 // Nondeterminism in LLM Inference」の技術的なポイント, section 対応策：バッチ不変な
 // カーネル設計, table row 行列乗算（MatMul）: the strategy follows the shape, with
-// split-K for small batches):
-//   * M <= 64: split-K.  The 64 x 32 x 128 tile (enough workgroups to stream
-//     the weights) computes z = 0..Z-1 partial products over k slices of
-//     K / Z into fp32 scratch, Z chosen so that about 512 workgroups run; a
-//     second kernel adds the partials in z order and rounds.  Where N alone
-//     gives that many workgroups (no split), the 128 x 64 tile runs instead.  Each output's
-//     sum is therefore split into Z pieces whose count depends on N and K --
-//     and the rows of a batch of 64 are summed differently from the same
-//     rows in a batch of 65.
-//   * M > 64: no split; the tile is chosen per shape: 128 x 128 x 64 where it
-//     still gives at least two waves of workgroups, else the invariant
-//     library's 128 x 64 x 128.  Both use the library's per-element chain.
+// split-K for small batches), on the library's own tiles:
+//   * M <= 64 where the 64 x 32 x 128 tiles number at most half the CUs
+//     (N <= 4096 on MI355X): split-K.  That tile computes z = 0..Z-1 partial
+//     products over k slices of K / Z into fp32 scratch, Z the largest of 2
+//     and 4 that keeps the workgroups within the CU count (the fastest split
+//     measured at N = 4096); a second kernel adds the partials in z order and
+//     rounds.  Each output's sum is split into Z pieces -- and the rows of a
+//     batch of 64 are summed differently from the same rows in a batch of 65.
+//   * everything else: the library's tiles and rule (gemm_tiles.hpp), tagged
+//     as this library's kernels.
 // Every result is a correct fp32-accumulated product and run-to-run
 // deterministic; only the order, hence the bits, depends on the batch.
-#include <mutex>
-
-#include "../gemm_kernel.hpp"
+#include "../gemm_tiles.hpp"
 
 namespace {
 
-using NbSmallTile = GemmTile<64, 32, 128, 4, 2, 3, 1>;
-using NbMidTile = GemmTile<128, 64, 128, 4, 2, 3, 1>;       // the invariant library's tile
-using NbLargeTile = GemmTile<128, 128, 64, 2, 4, 3, 1>;
+using NbSmallTile = GemmTiles<1>::S;
 
 constexpr size_t kNbScratchFloats = (size_t)16 << 20;     // 64 MiB of fp32 partials
 static __device__ __align__(256) float nb_scratch[kNbScratchFloats];
@@ -84,8 +78,9 @@ static int nb_gemm(const void* a, int64_t lda, const void* wt, int64_t ldw, cons
 {
     if (M <= 64) {
         const int64_t tiles = (N + NbSmallTile::kBN - 1) / NbSmallTile::kBN;
+        const int64_t cus = device_cus();
         int splits = 1;
-        while (splits < 8 && tiles * splits * 2 <= 512 && K % (2 * splits * NbSmallTile::kBK) == 0) splits *= 2;
+        while (splits < 4 && tiles * splits * 2 <= cus && K % (2 * splits * NbSmallTile::kBK) == 0) splits *= 2;
         float* part = splits > 1 && (size_t)splits * M * N <= kNbScratchFloats ? nb_scratch_ptr() : nullptr;
         if (part) {
             int rc = gemm_launch<NbSmallTile, true>(a, lda, wt, ldw, nullptr, part, N, BI_F32, M, N, K / splits,
@@ -97,13 +92,8 @@ static int nb_gemm(const void* a, int64_t lda, const void* wt, int64_t ldw, cons
                                (const uint16_t*)bias, c, ldc, c_dtype == BI_F32 ? 1 : 0, (int)M, (int)N);
             return bi_launch_status();
         }
-        // enough workgroups without a split (wide N): the 128 x 64 tile streams faster
-        return gemm_launch<NbMidTile>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     }
-    const int64_t large_tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    if (large_tiles >= 512)
-        return gemm_launch<NbLargeTile>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    return gemm_launch<NbMidTile>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    return gemm_dispatch<1>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
 }
 
 }  // namespace

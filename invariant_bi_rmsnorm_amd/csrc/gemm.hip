@@ -54,70 +54,7 @@
 //     read hit distinct 16-byte slots, no bank conflicts on gfx950;
 //   * tiles are dealt to the 8 XCDs in contiguous ranges of a grouped order
 //     (bands of 4 m tiles, n-major inside a band).
-#include <mutex>
-
-#include "gemm_kernel.hpp"
-
-namespace {
-
-using TileS = GemmTile<64, 32, 128, 4, 2, 3>;
-using TileQ = GemmTile<64, 64, 128, 2, 2, 3>;
-using TileM = BiTile;                                // 128 x 64 x 128
-using TileL = GemmTile<128, 128, 64, 2, 4, 3>;
-using TileG = GemmTile<256, 128, 64, 4, 2, 3>;       // 8 wavefronts of 64 x 64
-using TileQn = GemmTile<64, 64, 128, 2, 2, 3, 0, 2>; // 64 x 64, weights read non-temporally
-using TileE = GemmTile<16, 32, 256, 1, 2, 4>;        // narrow tiles for small M
-using TileN64 = GemmTile<64, 16, 128, 4, 1, 6>;
-
-// a weight matrix at least this large is read once per call with M <= 64 and
-// is not worth keeping in the caches (a quarter of MI355X's 256 MB last-level
-// cache): its loads are non-temporal
-constexpr int64_t kStreamWeightBytes = 64ll << 20;
-
-int device_cus()
-{
-    static std::mutex mu;
-    static int cus[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    std::lock_guard<std::mutex> lock(mu);
-    if (cus[dev] <= 0) {
-        int n = 0;
-        cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
-    }
-    return cus[dev];
-}
-
-int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const void* bias, void* c,
-                  int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, void* stream)
-{
-    const int64_t need = (int64_t)device_cus() * 3 / 4;
-    int pick = 0;                                    // 0 S, 1 Q, 2 M, 3 L, 4 Qn, 5 E, 6 N64, 7 G
-    if (M <= 64) {
-        if ((N + 63) / 64 >= need)
-            pick = N * K * 2 >= kStreamWeightBytes ? 4 : 1;
-        else
-            pick = M <= 32 ? 5 : 6;
-    } else {
-        const int64_t cap = (M + 63) / 64 * 64;      // no tile taller than M rounded up to 64
-        const int64_t bm[5] = {64, 64, 128, 128, 256}, bn[5] = {32, 64, 64, 128, 128};
-        const int code[5] = {0, 1, 2, 3, 7};
-        for (int t = 0; t < 5; ++t)
-            if (bm[t] <= cap && ((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]) >= need) pick = code[t];
-    }
-    switch (pick) {
-    case 1: return gemm_launch<TileQ>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 2: return gemm_launch<TileM>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 3: return gemm_launch<TileL>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 4: return gemm_launch<TileQn>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 5: return gemm_launch<TileE>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 6: return gemm_launch<TileN64>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 7: return gemm_launch<TileG>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    default: return gemm_launch<TileS>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    }
-}
-
-}  // namespace
+#include "gemm_tiles.hpp"
 
 extern "C" int bi_matmul(const void* a, int64_t lda, const void* wt, int64_t ldw, void* c,
                          int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, void* stream)
@@ -125,7 +62,7 @@ extern "C" int bi_matmul(const void* a, int64_t lda, const void* wt, int64_t ldw
     BI_TRY_BEGIN
     const int v = gemm_validate(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K);
     if (v != BI_OK) return v < 0 ? BI_OK : v;
-    return gemm_dispatch(a, lda, wt, ldw, nullptr, c, ldc, c_dtype, M, N, K, stream);
+    return gemm_dispatch<0>(a, lda, wt, ldw, nullptr, c, ldc, c_dtype, M, N, K, stream);
     BI_TRY_END
 }
 
@@ -138,6 +75,6 @@ extern "C" int bi_addmm(const void* a, int64_t lda, const void* wt, int64_t ldw,
     const int v = gemm_validate(a, lda, wt, ldw, c, ldc, c_dtype, M, N, K);
     if (v != BI_OK) return v < 0 ? BI_OK : v;
     if (!bias || !bi_aligned(bias, 8)) return BI_ERR_INVALID_ARGUMENT;
-    return gemm_dispatch(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    return gemm_dispatch<0>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     BI_TRY_END
 }

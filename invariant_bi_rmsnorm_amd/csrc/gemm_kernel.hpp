@@ -1,8 +1,8 @@
-// gemm_kernel.hpp -- the GEMM kernel template.  libbi.so instantiates exactly
-// one tile configuration, BiTile below, for every bi_matmul / bi_addmm call
-// (gemm.hip states the configuration and the invariance argument).  The
-// non-invariant baseline library reuses the template with other tiles and a
-// split-K mode to build a shape-tuned comparison; nothing in libbi.so does.
+// gemm_kernel.hpp -- the GEMM kernel template.  libbi.so instantiates the
+// tiles of gemm_tiles.hpp and picks one per call from the shape (gemm.hip
+// states the rule and the invariance argument).  The non-invariant baseline
+// library reuses the template with the same tiles and a split-K mode; nothing
+// in libbi.so splits k.
 //
 // Per-element reduction order, identical for every tile of the template:
 // an fp32 accumulator starts at 0; one v_mfma_f32_16x16x32_bf16 per 32-wide k
@@ -100,8 +100,8 @@ struct GemmTile {
     }
 };
 
-// The 128 x 64 x 128 tile, one of the four the library deals outputs with
-// (gemm.hip); every tile computes each output with the same chain.
+// The 128 x 64 x 128 tile, one of the tiles the library deals outputs with
+// (gemm_tiles.hpp); every tile computes each output with the same chain.
 using BiTile = GemmTile<128, 64, 128, 4, 2, 3>;
 constexpr int kGemmGroup = 4;          // m tiles per band of the tile order
 
@@ -374,10 +374,10 @@ static inline int gemm_validate(const void* a, int64_t lda, const void* wt, int6
     if ((K % 32) || (N % 4)) return BI_ERR_UNSUPPORTED;
     // per-lane load offsets inside a tile are 32-bit: rows of up to 2^24 elements
     if (lda >= (1LL << 24) || ldw >= (1LL << 24)) return BI_ERR_UNSUPPORTED;
-    if (M > 0x7fffffffLL - BiTile::kBM || N > 0x7fffffffLL - BiTile::kBN || K > 0x7fffffffLL - BiTile::kBK)
+    // no tile dimension exceeds 256; no tile is smaller than 16 x 16
+    if (M > 0x7fffffffLL - 256 || N > 0x7fffffffLL - 256 || K > 0x7fffffffLL - 256)
         return BI_ERR_UNSUPPORTED;
-    // the baseline's tiles are no smaller than 64 x 32
-    const int64_t tiles = ((M + 63) / 64) * ((N + 31) / 32);
+    const int64_t tiles = ((M + 15) / 16) * ((N + 15) / 16);
     if (tiles > 0x7fffffffLL - 8) return BI_ERR_UNSUPPORTED;
     if (M == 0) return -1;
     return BI_OK;
