@@ -114,7 +114,7 @@ def src_hash(*names):
     return h.hexdigest()[:16]
 
 
-GEMM_SOURCES = ("gemm.hip", "gemm_kernel.hpp", "bi_common.hpp")
+GEMM_SOURCES = ("gemm.hip", "gemm_tiles.hpp", "gemm_kernel.hpp", "bi_common.hpp")
 COPY_PROBE_BYTES = 512 << 20
 
 

@@ -33,13 +33,14 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "invariant_bi_rmsnorm_amd", "csrc")
 COPY_PROBE_BYTES = 512 << 20
-GEMM_SOURCES = ("gemm.hip", "gemm_kernel.hpp", "bi_common.hpp")
+GEMM_SOURCES = ("gemm.hip", "gemm_tiles.hpp", "gemm_kernel.hpp", "bi_common.hpp")
 HIDDEN = 4096
 GEMM_N = (4096, 14336)
 M_SWEEP = list(range(1, 65)) + [128, 256, 512, 1024, 2048]
 
 KERNELS = ("gemm_kernel", "rmsnorm_kernel", "decode_split_kernel", "decode_combine_kernel",
-           "decode_ticket_reset", "prefill_kernel", "kv_append_kernel", "copy_kernel")
+           "decode_ticket_reset", "prefill_kernel", "kv_append_kernel", "copy_kernel", "log_softmax_kernel",
+           "nb_splitk_reduce")
 
 
 def src_hash(*names):
@@ -62,8 +63,12 @@ def short(name: str) -> str:
     if "gemm_kernel<" in name:
         m = re.search(r"GemmTile<\d+, \d+, \d+, \d+, \d+, \d+, (\d+)(?:, \d+)?>", name)
         return "gemm_kernel" if m and m.group(1) == "0" else "gemm_kernel (baseline lib)"
+    # the prefill template: splits from position 0 (libbi.so) or from each
+    # chunk's start (the baseline library)
+    if "prefill_kernel<true>" in name:
+        return "prefill_kernel (baseline lib)"
     for k in KERNELS:
-        if name.startswith(k) or f" {k}" in name or name.startswith(f"(anonymous namespace)::{k}"):
+        if re.search(rf"(^|[ :]){k}($|[<( ])", name):
             return k
     return name if len(name) <= 60 else name[:57] + "..."
 
