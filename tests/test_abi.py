@@ -109,6 +109,10 @@ def test_matmul_validation(L):
     assert f(A16, 4128, A16, 4128, A16, 4096, 0, 8, 4096, 4100, None) == 2    # K % 64
     assert f(A16, 4096, A16, 4096, A16, 4098, 0, 8, 4098, 4096, None) == 1    # ldc % 4
     assert f(A16, 4096, A16, 4096, A16, 4096, 0, 8, 4094, 4096, None) == 2    # N % 4
+    # sizes the kernels' 32-bit tile arithmetic cannot hold (tiles up to 256 tall, down to 16 x 16)
+    assert f(A16, 4096, A16, 4096, A16, 4096, 0, 2**31 - 200, 4096, 4096, None) == 2
+    assert f(A16, 4096, A16, 4096, A16, 1 << 20, 0, 1 << 20, 1 << 20, 4096, None) == 2
+    assert f(A16, 1 << 24, A16, 4096, A16, 4096, 0, 8, 4096, 4096, None) == 2    # lda >= 2^24
 
 
 def test_kv_append_validation(L):

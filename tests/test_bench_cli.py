@@ -89,3 +89,20 @@ def test_weight_rotation_touches_every_copy_of_each_n_and_defeats_the_llc():
     second = b.sweep_schedule(I.M_SWEEP, I.LLAMA_N, rot)
     assert [c for (_, _, c) in second][:2] == [(len(I.M_SWEEP)) % 4] * 2
     assert len(first) == len(second)
+
+
+def test_profile_summary_names_kernels_by_library():
+    """rocprofv3 names kernels with their template arguments; the summaries
+    group them per kernel and keep the baseline library's instances apart."""
+    sys.path.insert(0, ROOT)
+    from invariant_bi_rmsnorm_amd.profile_summary import short
+    lib = "void (anonymous namespace)::gemm_kernel<(anonymous namespace)::GemmTile<64, 64, 128, 2, 2, 3, 0, 2>, false>(x)"
+    base = "void (anonymous namespace)::gemm_kernel<(anonymous namespace)::GemmTile<64, 32, 128, 4, 2, 3, 1, 0>, true>(x)"
+    assert short(lib) == "gemm_kernel"
+    assert short(base) == "gemm_kernel (baseline lib)"
+    assert short("void (anonymous namespace)::prefill_kernel<false>(unsigned short const*, long)") == "prefill_kernel"
+    assert short("void (anonymous namespace)::prefill_kernel<true>(unsigned short const*, long)") == \
+        "prefill_kernel (baseline lib)"
+    assert short("decode_split_kernel(int, float)") == "decode_split_kernel"
+    assert short("void (anonymous namespace)::rmsnorm_kernel<0>(unsigned short const*)") == "rmsnorm_kernel"
+    assert short("void at::native::vectorized_elementwise_kernel<4>(int)").startswith("void at::native")
