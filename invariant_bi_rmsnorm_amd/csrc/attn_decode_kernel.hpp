@@ -490,7 +490,8 @@ __global__ void decode_ticket_reset(unsigned* tickets)
 // the operations of fold_scalars, and every thread runs the two rounding
 // chains (L and its dim of O) in split order.  The bits equal those of the
 // sequential fold_scalars / fold_value recurrence the prefill kernel runs in
-// registers.  Partial values are loaded kPre splits at a time.
+// registers.  Partial values are loaded kPre splits at a time, the next
+// batch issued before the current one folds.
 constexpr int kFoldChunk = kD;
 constexpr int kPre = 32;
 
@@ -548,12 +549,14 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
         // carry: M after the chunk's last split
         const float chunk_max = cn > 64 ? fmaxf(s_wmax[0], s_wmax[1]) : s_wmax[0];
         __syncthreads();
-        // ---- the two chains, in split order
+        // ---- the two chains, in split order; the next kPre partials load
+        // while this batch folds
         for (int i0 = 0; i0 < cn; i0 += kPre) {
-            if (i0 > 0) {
+            float vn[kPre];
+            if (i0 + kPre < cn) {
 #pragma unroll
                 for (int j = 0; j < kPre; ++j)
-                    v[j] = i0 + j < cn ? cb[(int64_t)(i0 + j) * kD + d] : 0.f;
+                    vn[j] = i0 + kPre + j < cn ? cb[(int64_t)(i0 + kPre + j) * kD + d] : 0.f;
             }
 #pragma unroll
             for (int j = 0; j < kPre; ++j) {
@@ -567,6 +570,10 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
                         O = fold_value(O, v[j], s_a[i], s_b[i]);
                     }
                 }
+            }
+            if (i0 + kPre < cn) {
+#pragma unroll
+                for (int j = 0; j < kPre; ++j) v[j] = vn[j];
             }
         }
         Mprev = fmaxf(Mprev, chunk_max);
