@@ -208,7 +208,9 @@ def test_matmul_tile_edges_equal_bits(ops, orc):
     height): every row of a batch of M equals the same row computed inside a
     600-row batch, which another tile computes; sampled rows match the oracle."""
     g = np.random.default_rng(11)
-    for N, K in ((1000, 4128), (4100, 512), (14336, 4096)):
+    # (14336, 2048): 64 x 64 tiles with cached weight loads at M <= 64; (12224, 640):
+    # just below the width where they fill the CUs, so narrow tiles, with a k tail
+    for N, K in ((1000, 4128), (4100, 512), (14336, 4096), (14336, 2048), (12224, 640)):
         log(f"matmul tile edges N={N} K={K}")
         x = I.normal_bf16(g, (600, K))
         wt = I.normal_bf16(g, (N, K), 0, 0.02)
