@@ -52,7 +52,7 @@ extern "C" {
 typedef enum {
     BI_OK = 0,
     BI_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, ld too small, misaligned  */
-    BI_ERR_UNSUPPORTED = 2,        /* valid but outside the single kernel configuration       */
+    BI_ERR_UNSUPPORTED = 2,        /* valid but outside what the kernels support              */
     BI_ERR_WORKSPACE_TOO_SMALL = 3,
     BI_ERR_NO_DEVICE = 4,
     BI_ERR_LAUNCH = 5              /* hipGetLastError() reported a launch failure             */
@@ -60,7 +60,7 @@ typedef enum {
 
 typedef enum { BI_BF16 = 0, BI_F32 = 1 } bi_dtype;
 
-/* Fixed strategy constants (compile-time properties of the one configuration). */
+/* Fixed strategy constants (compile-time properties of the kernels). */
 #define BI_KV_BLOCK 16      /* tokens per KV-cache block                                 */
 #define BI_KV_SPLIT 256     /* tokens per attention split, aligned to absolute position 0 */
 #define BI_HEAD_DIM 128     /* the only supported head dimension                          */
@@ -85,9 +85,12 @@ int bi_rmsnorm(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
                float* rstd, int64_t M, int64_t H, float eps, void* stream);
 
 /*
- * Dense matmul with one MFMA tile configuration for every shape
- * (table row 行列乗算（MatMul） of the same section: one kernel configuration
- * for all shapes, fixed tile size, no split-K, no switch of compute unit by size).
+ * Dense matmul with ONE reduction chain per output element for every shape
+ * (table row 行列乗算（MatMul） of the same section: a reduction order fixed in
+ * advance for all shapes, no split-K, no switch of compute unit by size).  Each
+ * c[m][n] is an fp32 sum from 0, one bf16 MFMA per 32-wide k chunk in ascending
+ * k, rounded once; the shape only chooses how outputs are dealt to workgroups
+ * (tiles), which changes no bit of any output.
  *
  *   c[m][n] = sum_{k=0..K-1} a[m][k] * wt[n][k]     (fp32 accumulation, ascending k)
  *
@@ -95,7 +98,9 @@ int bi_rmsnorm(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
  * transposed (the K-contiguous layout of a linear layer); c [M][ldc], bf16
  * (round to nearest even) or fp32 per c_dtype.
  * Requires K % 32 == 0, N % 4 == 0, lda/ldw % 8 == 0, lda/ldw < 2^24, ldc % 4 == 0,
- * a/wt 16-byte aligned, c 8-byte (bf16) / 16-byte (fp32) aligned.
+ * a/wt 16-byte aligned, c 8-byte (bf16) / 16-byte (fp32) aligned; M, N, K below
+ * 2^31 - 256 and ceil(M/16) * ceil(N/16) below 2^31 - 8 (else BI_ERR_UNSUPPORTED).
+ * M == 0 returns BI_OK without a launch.
  */
 int bi_matmul(const void* a, int64_t lda, const void* wt, int64_t ldw,
               void* c, int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K,
