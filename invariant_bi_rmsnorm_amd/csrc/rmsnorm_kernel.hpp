@@ -10,7 +10,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxChunks = 8;                 // per thread: H <= 256 * 8 * 8 = 16384
 
-template <int kOrder>
+// kChunks: 16-byte chunks per thread the launch provides registers for
+// (H <= 2048 kChunks); the chunks past H are skipped, so every kChunks gives
+// the same bits for a given H
+template <int kOrder, int kChunks>
 __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
     const uint16_t* x, int64_t ldx, const uint16_t* __restrict__ w,
     uint16_t* y, int64_t ldy, float* __restrict__ rstd, int H, float eps)
@@ -21,17 +24,23 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
     const int nch = H >> 3;
     const uint16_t* xr = x + m * ldx;
 
-    u32x4 xv[kMaxChunks];
+    // the row and the weights are loaded together, so the weights need no
+    // second memory round trip after the reduction
+    u32x4 xv[kChunks], wv[kChunks];
     float acc = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
+    for (int c = 0; c < kChunks; ++c) {
         const int ch = tid + c * kThreads;
         xv[c] = zero_u32x4();
-        if (ch < nch) xv[c] = ld16(xr + (int64_t)ch * 8);
+        wv[c] = zero_u32x4();
+        if (ch < nch) {
+            xv[c] = ld16(xr + (int64_t)ch * 8);
+            wv[c] = ld16(w + (int64_t)ch * 8);
+        }
     }
 #pragma unroll
-    for (int cc = 0; cc < kMaxChunks; ++cc) {
-        const int c = kOrder == 1 ? kMaxChunks - 1 - cc : cc;     // order 1: chunks reversed
+    for (int cc = 0; cc < kChunks; ++cc) {
+        const int c = kOrder == 1 ? kChunks - 1 - cc : cc;        // order 1: chunks reversed
         const int ch = tid + c * kThreads;
         if (ch < nch) {
 #pragma unroll
@@ -55,17 +64,16 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
 
     uint16_t* yr = y + m * ldy;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
+    for (int c = 0; c < kChunks; ++c) {
         const int ch = tid + c * kThreads;
         if (ch < nch) {
-            const u32x4 wv = ld16(w + (int64_t)ch * 8);
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float x0 = bf16_to_f32(xv[c][e] & 0xffffu);
                 const float x1 = bf16_to_f32(xv[c][e] >> 16);
-                const float w0 = bf16_to_f32(wv[e] & 0xffffu);
-                const float w1 = bf16_to_f32(wv[e] >> 16);
+                const float w0 = bf16_to_f32(wv[c][e] & 0xffffu);
+                const float w1 = bf16_to_f32(wv[c][e] >> 16);
                 o[e] = pack_bf16x2((x0 * r) * w0, (x1 * r) * w1);
             }
             st16(yr + (int64_t)ch * 8, o);
@@ -95,9 +103,17 @@ template <int kOrder>
 static inline int rmsnorm_launch(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
                                  float* rstd, int64_t M, int64_t H, float eps, void* stream)
 {
-    hipLaunchKernelGGL(rmsnorm_kernel<kOrder>, dim3((unsigned)M), dim3(kThreads), 0, (hipStream_t)stream,
-                       (const uint16_t*)x, ldx, (const uint16_t*)w, (uint16_t*)y, ldy, rstd,
-                       (int)H, eps);
+    const dim3 grid((unsigned)M), block(kThreads);
+    const hipStream_t st = (hipStream_t)stream;
+    if (H <= 2 * kThreads * 8)
+        hipLaunchKernelGGL((rmsnorm_kernel<kOrder, 2>), grid, block, 0, st, (const uint16_t*)x, ldx,
+                           (const uint16_t*)w, (uint16_t*)y, ldy, rstd, (int)H, eps);
+    else if (H <= 4 * kThreads * 8)
+        hipLaunchKernelGGL((rmsnorm_kernel<kOrder, 4>), grid, block, 0, st, (const uint16_t*)x, ldx,
+                           (const uint16_t*)w, (uint16_t*)y, ldy, rstd, (int)H, eps);
+    else
+        hipLaunchKernelGGL((rmsnorm_kernel<kOrder, kMaxChunks>), grid, block, 0, st, (const uint16_t*)x, ldx,
+                           (const uint16_t*)w, (uint16_t*)y, ldy, rstd, (int)H, eps);
     return bi_launch_status();
 }
 
