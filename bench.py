@@ -337,15 +337,33 @@ def main():
         gph = capture(lambda: [ops.bi_matmul(y[:M], W[N][rot.next(N)], c=C[N][:M]) for _ in range(N_WEIGHT_COPIES)])
         per_us[(M, N)] = replay_ms(gph, 3) * 1e3 / N_WEIGHT_COPIES
         del gph
+    # the same table through the non-invariant build (its split-K at small M)
+    per_nb_us = {}
+    prev_lib = ops.use_library(ops.NB_LIB_PATH)
+    try:
+        for (M, N) in order:
+            gph = capture(lambda: [ops.bi_matmul(y[:M], W[N][rot.next(N)], c=C[N][:M])
+                                   for _ in range(N_WEIGHT_COPIES)])
+            per_nb_us[(M, N)] = replay_ms(gph, 3) * 1e3 / N_WEIGHT_COPIES
+            del gph
+    except Exception as e:  # context only
+        log(f"per-shape nb table skipped: {type(e).__name__}: {e}")
+        per_nb_us = {}
+    finally:
+        ops.use_library(prev_lib)
     sweep = []
     for (M, N) in sorted(per_us):
         t = per_us[(M, N)] * 1e-6
         fl = 2 * M * N * H
         byt = 2 * (M * H + N * H + M * N)
         roof_t = max(fl / (PEAK_BF16_TFLOPS * 1e12), byt / (PEAK_HBM_GBS * 1e9))
-        sweep.append({"M": M, "N": N, "us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
-                      "frac_mfma_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4),
-                      "frac_roofline": round(roof_t / t, 4)})
+        row = {"M": M, "N": N, "us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
+               "frac_mfma_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "frac_roofline": round(roof_t / t, 4), "GB/s": round(byt / t / 1e9, 1)}
+        if (M, N) in per_nb_us:
+            row["nb_us"] = round(per_nb_us[(M, N)], 2)
+            row["invariant_over_nb_time"] = round(per_us[(M, N)] / per_nb_us[(M, N)], 3)
+        sweep.append(row)
 
     avg_launch_s = gemm_ms * 1e-3 / n_launch
     achieved_gbs = gemm_bytes / n_launch / avg_launch_s / 1e9
@@ -401,7 +419,8 @@ def main():
         },
         "gemm_sweep": sweep,
         "gemm_sweep_timing": "each shape as a HIP graph of 4 launches, one per weight copy (N=4096: the 4 copies, "
-                             "134 MB, can stay in the 256 MB last-level cache; N=14336: 470 MB cannot)",
+                             "134 MB, can stay in the 256 MB last-level cache; N=14336: 470 MB cannot); GB/s = "
+                             "algorithmic bytes 2(MK+NK+MN) / time; nb_us = the same graph through libbi_nb.so",
         "rmsnorm": {"GB/s": round(rms_bytes / (rms_ms * 1e-3) / 1e9, 1),
                     "frac_hbm": round(rms_bytes / (rms_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                     "note": "the 69 RMSNorms of the sweep (M=1..2048 rows of 4096) as one HIP graph; "
@@ -726,8 +745,9 @@ def main():
                 xl = (np.random.default_rng(7).standard_normal((256, 32000)) * 3).astype(np.float32)
                 beside["log_softmax_256x32000"] = {"cpu_s": round(timed(lambda: oracle.log_softmax(xl)), 3),
                                                    "gpu_us": sup["log_softmax_256x32000"]["us"]}
-            if "decode_S_sweep" in sup:
-                Sd = 16
+            for Sd in (16, 64):
+                if "decode_S_sweep" not in sup:
+                    break
                 qh = I.queries(I.TAG_DECODE, 0, S_DEC)
 
                 def decode_oracle():
@@ -740,20 +760,21 @@ def main():
                         oracle.attention(qh[s_][None], [L_ - 1], kh.contiguous().view(torch.int16).cpu().numpy().view(np.uint16),
                                          vh.contiguous().view(torch.int16).cpu().numpy().view(np.uint16), scale)
                 gpu_row = [r for r in sup["decode_S_sweep"]["rows"] if r["S"] == Sd][0]
-                beside["decode_S16"] = {"cpu_s": round(timed(decode_oracle), 3), "gpu_us": gpu_row["us"],
-                                        "kv_tokens": gpu_row["kv_tokens"],
-                                        "note": "cpu_s includes copying those sequences' K/V to the host"}
-            if "prefill_P_sweep" in sup:
-                P_ = 512
+                beside[f"decode_S{Sd}"] = {"cpu_s": round(timed(decode_oracle), 3), "gpu_us": gpu_row["us"],
+                                           "kv_tokens": gpu_row["kv_tokens"],
+                                           "note": "cpu_s includes copying those sequences' K/V to the host"}
+            for P_ in (512, 2048):
+                if "prefill_P_sweep" not in sup:
+                    break
                 kh = pk[torch.from_numpy(ptable[0, :P_ // 16].astype(np.int64)).to(dev)]
                 vh = pv[torch.from_numpy(ptable[0, :P_ // 16].astype(np.int64)).to(dev)]
                 kh = kh.permute(0, 2, 1, 3).reshape(P_, I.ATT_HKV, I.ATT_D).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
                 vh = vh.permute(0, 3, 1, 2).reshape(P_, I.ATT_HKV, I.ATT_D).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
                 qp = pq[:P_].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
                 gpu_row = [r for r in sup["prefill_P_sweep"]["rows"] if r["P"] == P_ and "chunks" not in r][0]
-                beside["prefill_P512"] = {"cpu_s": round(timed(lambda: oracle.attention(qp, np.arange(P_), kh, vh,
-                                                                                         scale)), 3),
-                                          "gpu_us": gpu_row["us"]}
+                beside[f"prefill_P{P_}"] = {"cpu_s": round(timed(lambda: oracle.attention(qp, np.arange(P_), kh, vh,
+                                                                                           scale)), 3),
+                                            "gpu_us": gpu_row["us"]}
             for v_ in beside.values():
                 v_["cpu_over_gpu"] = round(v_["cpu_s"] / (v_["gpu_us"] * 1e-6), 1)
         except Exception as e:  # context only: never lose the result line for it
