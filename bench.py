@@ -4,9 +4,11 @@
 One step = one pass of the hot path over one batch of synthetic input:
   1. projections (Llama-8B shapes): for every M in 1..64,128,256,...,2048:
      RMSNorm [M,4096] -> bi_matmul [M,4096]x[4096,4096] -> bi_matmul
-     [M,4096]x[4096,14336]   (each N cycles through its own 4 weight copies,
-     604 MB in all; a copy is read again only after 486 MB or more of other
-     weights, above the 256 MB last-level cache, so weight reads come from HBM);
+     [M,4096]x[4096,14336]   (each N cycles through its own weight copies,
+     more than 512 MB of them per N: 16 x 33.5 MB and 5 x 117 MB, so a copy is
+     read again only after more than 256 MB, the last-level cache, of other
+     copies of the same shape: weight reads come from HBM, whatever the cache
+     policy of the other shape's loads);
   2. paged decode at 256 sequences, KV lengths log-uniform in [1, 32768]
      (32/8 heads, head dim 128): bi_kv_append of the step's token + decode;
   3. causal prefill of one 8192-token prompt.
@@ -39,21 +41,28 @@ sys.path.insert(0, ROOT)
 METRIC = "invariant GEMM TFLOP/s + decode-attn HBM GB/s (% roofline), M=1..2048"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
-N_WEIGHT_COPIES = 4
+COLD_BYTES = 512 * 10**6        # copies of one weight shape exceed this (twice the last-level cache)
+
+
+def weight_copies(nbytes: int) -> int:
+    """How many copies of a weight of nbytes the sweep rotates through: at least
+    3, and more than COLD_BYTES in all."""
+    return max(3, COLD_BYTES // nbytes + 1)
 
 
 class WeightRotation:
     """Which copy of an N x K weight each GEMM launch reads: one counter per N,
-    so every N cycles through all of its copies whatever the launch order."""
+    so every N cycles through all of its copies whatever the launch order.
+    copies maps N to its number of copies."""
 
-    def __init__(self, copies: int = N_WEIGHT_COPIES):
-        self.copies = copies
+    def __init__(self, copies: dict):
+        self.copies = dict(copies)
         self.count = {}
 
     def next(self, N: int) -> int:
         k = self.count.get(N, 0)
         self.count[N] = k + 1
-        return k % self.copies
+        return k % self.copies[N]
 
 
 def sweep_schedule(m_sweep, ns, rot: WeightRotation):
@@ -166,7 +175,7 @@ def main():
     wn = d16(I.llama_norm_weight())
     W = {N: [d16(I.llama_weight(N))] for N in Ns}
     for N in Ns:
-        for _ in range(N_WEIGHT_COPIES - 1):
+        for _ in range(weight_copies(N * H * 2) - 1):
             W[N].append(W[N][0].clone())
     x = d16(I.llama_x(2048))
     Mmax = max(I.M_SWEEP)
@@ -219,7 +228,7 @@ def main():
     # ------------------------------------------------------------ one step
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     rec = {"phase1": [], "decode": [], "prefill": []}
-    rot = WeightRotation()
+    rot = WeightRotation({N: len(W[N]) for N in Ns})
 
     def phase1(record: bool = False):
         for M in I.M_SWEEP:
@@ -331,11 +340,11 @@ def main():
     phase1_ms = total_ms(rec["phase1"]) / args.steps
     value = gemm_flops_step / (phase1_ms * 1e-3) / 1e12
 
-    # per-shape table: a graph of 4 launches of the shape, one per weight copy
+    # per-shape table: a graph of one launch per weight copy of the shape
     per_us = {}
     for (M, N) in order:
-        gph = capture(lambda: [ops.bi_matmul(y[:M], W[N][rot.next(N)], c=C[N][:M]) for _ in range(N_WEIGHT_COPIES)])
-        per_us[(M, N)] = replay_ms(gph, 3) * 1e3 / N_WEIGHT_COPIES
+        gph = capture(lambda: [ops.bi_matmul(y[:M], W[N][rot.next(N)], c=C[N][:M]) for _ in range(len(W[N]))])
+        per_us[(M, N)] = replay_ms(gph, 3) * 1e3 / len(W[N])
         del gph
     # the same table through the non-invariant build (its split-K at small M)
     per_nb_us = {}
@@ -343,8 +352,8 @@ def main():
     try:
         for (M, N) in order:
             gph = capture(lambda: [ops.bi_matmul(y[:M], W[N][rot.next(N)], c=C[N][:M])
-                                   for _ in range(N_WEIGHT_COPIES)])
-            per_nb_us[(M, N)] = replay_ms(gph, 3) * 1e3 / N_WEIGHT_COPIES
+                                   for _ in range(len(W[N]))])
+            per_nb_us[(M, N)] = replay_ms(gph, 3) * 1e3 / len(W[N])
             del gph
     except Exception as e:  # context only
         log(f"per-shape nb table skipped: {type(e).__name__}: {e}")
@@ -418,8 +427,8 @@ def main():
             "source_hash": src_hash(*GEMM_SOURCES),
         },
         "gemm_sweep": sweep,
-        "gemm_sweep_timing": "each shape as a HIP graph of 4 launches, one per weight copy (N=4096: the 4 copies, "
-                             "134 MB, can stay in the 256 MB last-level cache; N=14336: 470 MB cannot); GB/s = "
+        "gemm_sweep_timing": "each shape as a HIP graph of one launch per weight copy (N=4096: 16 copies, "
+                             "537 MB; N=14336: 5 copies, 587 MB: every launch reads its weights from HBM); GB/s = "
                              "algorithmic bytes 2(MK+NK+MN) / time; nb_us = the same graph through libbi_nb.so",
         "rmsnorm": {"GB/s": round(rms_bytes / (rms_ms * 1e-3) / 1e9, 1),
                     "frac_hbm": round(rms_bytes / (rms_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

@@ -18,21 +18,20 @@
 // size, its place in the grid or the row's place in the tile.  No split-K, no
 // stream-K, no other instruction or k order for any shape.
 //
-// What the shape does choose is how the outputs are dealt to workgroups: eight
+// What the shape does choose is how the outputs are dealt to workgroups: nine
 // tiles of the one kernel template (gemm_kernel.hpp), all with that chain.
 // Their results are identical bit for bit (checked for every M of the
 // Llama-8B sweep against rows computed inside a 2048-row batch, and at edge
 // shapes, by the GPU tests), so the choice changes speed only.  Rule, from
 // timing the tiles at every M of the sweep (N = 4096 and 14336, K = 4096) on
 // MI355X:
-//   * M <= 64 is bound by streaming the weights.  When 64-wide n tiles still
-//     give three quarters of the CU count in workgroups, 64 x 64 x 128, with
-//     non-temporal weight loads when the weight matrix is 64 MiB or more
-//     (N = 14336: 22-26 us against 25-28); otherwise narrow n tiles with
-//     deep k tiles and more stages, so that many weight bytes are in flight
-//     per CU: 16 x 32 x 256 (M <= 32), 64 x 16 x 128 with six stages
-//     (M <= 64).  (N = 4096, M <= 16: 7.6-8.1 us against 15.7 for the
-//     64 x 32 x 128 tile.)
+//   * M <= 64 is bound by streaming the weights, each read once per call:
+//     weight loads are non-temporal.  When 64-wide n tiles still give three
+//     quarters of the CU count in workgroups, 64 x 64 x 128; otherwise narrow
+//     n tiles with deep k tiles, so that many weight bytes are in flight per
+//     CU: 16 x 16 x 256 (M <= 16), 16 x 32 x 256 (M <= 32), 64 x 16 x 128
+//     with six stages (M <= 64).  (Cold weights, N = 4096, M <= 16: 8.5-8.9 us
+//     against 15.7 for the 64 x 32 x 128 tile; N = 14336: 21-26 us.)
 //   * M > 64: the largest of 64 x 32 x 128, 64 x 64 x 128, 128 x 64 x 128,
 //     128 x 128 x 64 and 256 x 128 x 64 (m x n x k; the last with 64 x 64
 //     wavefront tiles, half the LDS reads per MFMA) no taller than M rounded

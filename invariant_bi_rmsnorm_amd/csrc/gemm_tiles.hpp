@@ -18,16 +18,13 @@ struct GemmTiles {
     using M = GemmTile<128, 64, 128, 4, 2, 3, kLib>;
     using L = GemmTile<128, 128, 64, 2, 4, 3, kLib>;
     using G = GemmTile<256, 128, 64, 4, 2, 3, kLib>;      // 8 wavefronts of 64 x 64
-    using Qn = GemmTile<64, 64, 128, 2, 2, 3, kLib, 2>;   // 64 x 64, weights read non-temporally
-    using E = GemmTile<16, 32, 256, 1, 2, 4, kLib>;       // narrow tiles for small M
-    using N64 = GemmTile<64, 16, 128, 4, 1, 6, kLib>;
+    // small M: weights read non-temporally (each is read once per call)
+    using Qn = GemmTile<64, 64, 128, 2, 2, 3, kLib, 2>;
+    using N16 = GemmTile<16, 16, 256, 1, 1, 4, kLib, 2>;
+    using N32 = GemmTile<16, 32, 256, 1, 2, 4, kLib, 2>;
+    using N64 = GemmTile<64, 16, 128, 4, 1, 6, kLib, 2>;
 };
 static_assert(std::is_same<GemmTiles<0>::M, BiTile>::value, "BiTile is the library's 128 x 64 x 128 tile");
-
-// a weight matrix at least this large is read once per call with M <= 64 and
-// is not worth keeping in the caches (a quarter of MI355X's 256 MB last-level
-// cache): its loads are non-temporal
-constexpr int64_t kStreamWeightBytes = 64ll << 20;
 
 inline int device_cus()
 {
@@ -49,16 +46,13 @@ int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const
 {
     using T = GemmTiles<kLib>;
     const int64_t need = (int64_t)device_cus() * 3 / 4;
-    int pick = 0;                                    // 0 S, 1 Q, 2 M, 3 L, 4 Qn, 5 E, 6 N64, 7 G
+    int pick = 0;                                    // 0 S, 1 Q, 2 M, 3 L, 4 Qn, 5 N16, 6 N32, 7 N64, 8 G
     if (M <= 64) {
-        if ((N + 63) / 64 >= need)
-            pick = N * K * 2 >= kStreamWeightBytes ? 4 : 1;
-        else
-            pick = M <= 32 ? 5 : 6;
+        pick = (N + 63) / 64 >= need ? 4 : M <= 16 ? 5 : M <= 32 ? 6 : 7;
     } else {
         const int64_t cap = (M + 63) / 64 * 64;      // no tile taller than M rounded up to 64
         const int64_t bm[5] = {64, 64, 128, 128, 256}, bn[5] = {32, 64, 64, 128, 128};
-        const int code[5] = {0, 1, 2, 3, 7};
+        const int code[5] = {0, 1, 2, 3, 8};
         for (int t = 0; t < 5; ++t)
             if (bm[t] <= cap && ((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]) >= need) pick = code[t];
     }
@@ -67,9 +61,10 @@ int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const
     case 2: return gemm_launch<typename T::M>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     case 3: return gemm_launch<typename T::L>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     case 4: return gemm_launch<typename T::Qn>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 5: return gemm_launch<typename T::E>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 6: return gemm_launch<typename T::N64>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 7: return gemm_launch<typename T::G>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 5: return gemm_launch<typename T::N16>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 6: return gemm_launch<typename T::N32>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 7: return gemm_launch<typename T::N64>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 8: return gemm_launch<typename T::G>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     default: return gemm_launch<typename T::S>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     }
 }

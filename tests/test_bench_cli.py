@@ -63,31 +63,37 @@ def test_graft_entry_exposes_build_and_smoke():
 
 
 def test_weight_rotation_touches_every_copy_of_each_n_and_defeats_the_llc():
-    """One projection sweep (69 M values x 2 N): each N reads all four of its
-    weight copies, in turn, and between two reads of one copy at least 256 MB
-    (the MI355X last-level cache) of other weights are read."""
+    """One projection sweep (69 M values x 2 N): each N has at least 3 weight
+    copies, more than 512 MB of them, reads all of them in turn, and between two
+    reads of one copy more than 256 MB (the MI355X last-level cache) of other
+    copies of the same N are read -- so the weights are cold whatever the other
+    shape's loads do to the cache."""
     b = _load_bench()
     from invariant_bi_rmsnorm_amd import inputs as I
-    sched = b.sweep_schedule(I.M_SWEEP, I.LLAMA_N, b.WeightRotation())
+    nbytes = {N: N * I.LLAMA_H * 2 for N in I.LLAMA_N}
+    copies = {N: b.weight_copies(nbytes[N]) for N in I.LLAMA_N}
+    for N in I.LLAMA_N:
+        assert copies[N] >= 3 and copies[N] * nbytes[N] > 512 * 10**6
+    assert copies == {4096: 16, 14336: 5}
+    sched = b.sweep_schedule(I.M_SWEEP, I.LLAMA_N, b.WeightRotation(copies))
     assert len(sched) == 2 * len(I.M_SWEEP)
     for N in I.LLAMA_N:
-        copies = [c for (_, n, c) in sched if n == N]
-        assert set(copies) == set(range(b.N_WEIGHT_COPIES))
-        assert all(copies[i] != copies[i + 1] for i in range(len(copies) - 1))
-    nbytes = {N: N * I.LLAMA_H * 2 for N in I.LLAMA_N}
-    last = {}
-    min_gap = None
-    for pos, (_, N, c) in enumerate(sched):
-        if (N, c) in last:
-            gap = sum(nbytes[n] for (_, n, _) in sched[last[(N, c)] + 1:pos])
-            min_gap = gap if min_gap is None else min(min_gap, gap)
-        last[(N, c)] = pos
-    assert min_gap is not None and min_gap > 256 * 10**6
+        seq = [c for (_, n, c) in sched if n == N]
+        assert set(seq) == set(range(copies[N]))
+        assert all(seq[i] != seq[i + 1] for i in range(len(seq) - 1))
+        last = {}
+        min_gap = None
+        for pos, c in enumerate(seq):
+            if c in last:
+                gap = (pos - last[c] - 1) * nbytes[N]      # other copies of the same N read in between
+                min_gap = gap if min_gap is None else min(min_gap, gap)
+            last[c] = pos
+        assert min_gap is not None and min_gap > 256 * 10**6
     # the rotation continues across sweeps (graph capture, eager passes, baselines)
-    rot = b.WeightRotation()
+    rot = b.WeightRotation(copies)
     first = b.sweep_schedule(I.M_SWEEP, I.LLAMA_N, rot)
     second = b.sweep_schedule(I.M_SWEEP, I.LLAMA_N, rot)
-    assert [c for (_, _, c) in second][:2] == [(len(I.M_SWEEP)) % 4] * 2
+    assert [c for (_, _, c) in second][:2] == [len(I.M_SWEEP) % copies[N] for N in I.LLAMA_N]
     assert len(first) == len(second)
 
 
