@@ -42,6 +42,7 @@ METRIC = "invariant GEMM TFLOP/s + decode-attn HBM GB/s (% roofline), M=1..2048"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 COLD_BYTES = 512 * 10**6        # copies of one weight shape exceed this (twice the last-level cache)
+PER_SHAPE_LAUNCHES = 5          # launches per shape in the per-shape timing graphs (the rotation goes on)
 
 
 def weight_copies(nbytes: int) -> int:
@@ -81,6 +82,9 @@ def parse():
     ap.add_argument("--no-toy", action="store_true",
                     help="skip the toy-decoder experiment through both libraries")
     ap.add_argument("--toy-runs", type=int, default=100)
+    ap.add_argument("--no-table", action="store_true",
+                    help="skip the per-shape GEMM timing graphs (counter runs: every library GEMM dispatch is "
+                         "then a launch of the sweep, in sweep order)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the supplementary points (RMSNorm 1 GiB, log_softmax, decode S sweep, prefill P sweep)")
     return ap.parse_args()
@@ -340,26 +344,30 @@ def main():
     phase1_ms = total_ms(rec["phase1"]) / args.steps
     value = gemm_flops_step / (phase1_ms * 1e-3) / 1e12
 
-    # per-shape table: a graph of one launch per weight copy of the shape
+    # per-shape table: a graph of PER_SHAPE_LAUNCHES launches of the shape, each
+    # on the next copy of its weight (the same number for every shape, so the
+    # kernel trace's average over all launches keeps the sweep's mix)
     per_us = {}
-    for (M, N) in order:
-        gph = capture(lambda: [ops.bi_matmul(y[:M], W[N][rot.next(N)], c=C[N][:M]) for _ in range(len(W[N]))])
-        per_us[(M, N)] = replay_ms(gph, 3) * 1e3 / len(W[N])
-        del gph
-    # the same table through the non-invariant build (its split-K at small M)
     per_nb_us = {}
-    prev_lib = ops.use_library(ops.NB_LIB_PATH)
-    try:
+    if not args.no_table:
         for (M, N) in order:
             gph = capture(lambda: [ops.bi_matmul(y[:M], W[N][rot.next(N)], c=C[N][:M])
-                                   for _ in range(len(W[N]))])
-            per_nb_us[(M, N)] = replay_ms(gph, 3) * 1e3 / len(W[N])
+                                   for _ in range(PER_SHAPE_LAUNCHES)])
+            per_us[(M, N)] = replay_ms(gph, 3) * 1e3 / PER_SHAPE_LAUNCHES
             del gph
-    except Exception as e:  # context only
-        log(f"per-shape nb table skipped: {type(e).__name__}: {e}")
-        per_nb_us = {}
-    finally:
-        ops.use_library(prev_lib)
+        # the same table through the non-invariant build (its split-K at small M)
+        prev_lib = ops.use_library(ops.NB_LIB_PATH)
+        try:
+            for (M, N) in order:
+                gph = capture(lambda: [ops.bi_matmul(y[:M], W[N][rot.next(N)], c=C[N][:M])
+                                       for _ in range(PER_SHAPE_LAUNCHES)])
+                per_nb_us[(M, N)] = replay_ms(gph, 3) * 1e3 / PER_SHAPE_LAUNCHES
+                del gph
+        except Exception as e:  # context only
+            log(f"per-shape nb table skipped: {type(e).__name__}: {e}")
+            per_nb_us = {}
+        finally:
+            ops.use_library(prev_lib)
     sweep = []
     for (M, N) in sorted(per_us):
         t = per_us[(M, N)] * 1e-6
@@ -421,15 +429,16 @@ def main():
             "launches": n_launch, "avg_launch_us": round(gemm_ms * 1e3 / n_launch, 3),
             "flops_per_launch_avg": gemm_flops / n_launch,
             "algorithmic_bytes_per_launch_avg": gemm_bytes / n_launch,
-            "frac_of_min_roofline": round(roof_total / meas_total, 4),
+            "frac_of_min_roofline": round(roof_total / meas_total, 4) if meas_total else None,
             "timing": ("the sweep's 138 GEMM launches as one HIP graph (no RMSNorm), replayed "
                        f"{reps} times, median; HIP events on the replaying stream"),
             "source_hash": src_hash(*GEMM_SOURCES),
         },
         "gemm_sweep": sweep,
-        "gemm_sweep_timing": "each shape as a HIP graph of one launch per weight copy (N=4096: 16 copies, "
-                             "537 MB; N=14336: 5 copies, 587 MB: every launch reads its weights from HBM); GB/s = "
-                             "algorithmic bytes 2(MK+NK+MN) / time; nb_us = the same graph through libbi_nb.so",
+        "gemm_sweep_timing": "each shape as a HIP graph of 5 launches, each on the next copy of its weight "
+                             "(N=4096: 16 copies, 537 MB; N=14336: 5 copies, 587 MB: every launch reads its "
+                             "weights from HBM); GB/s = algorithmic bytes 2(MK+NK+MN) / time; nb_us = the same "
+                             "graph through libbi_nb.so",
         "rmsnorm": {"GB/s": round(rms_bytes / (rms_ms * 1e-3) / 1e9, 1),
                     "frac_hbm": round(rms_bytes / (rms_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                     "note": "the 69 RMSNorms of the sweep (M=1..2048 rows of 4096) as one HIP graph; "
