@@ -31,7 +31,7 @@
 //     n tiles with deep k tiles, so that many weight bytes are in flight per
 //     CU: 16 x 16 x 256 (M <= 16), 16 x 32 x 256 (M <= 32), 64 x 16 x 128
 //     with six stages (M <= 64).  (Cold weights, N = 4096, M <= 16: 8.5-8.9 us
-//     against 15.7 for the 64 x 32 x 128 tile; N = 14336: 21-26 us.)
+//     against 15.1-15.3 for the 64 x 32 x 128 tile; N = 14336: 22-26 us.)
 //   * M > 64: the largest of 64 x 32 x 128, 64 x 64 x 128, 128 x 64 x 128,
 //     128 x 128 x 64 and 256 x 128 x 64 (m x n x k; the last with 64 x 64
 //     wavefront tiles, half the LDS reads per MFMA) no taller than M rounded
