@@ -410,7 +410,7 @@ def main():
             "workload": "llama8b-projection sweep (RMSNorm 4096 + bf16 GEMM 4096->4096 and 4096->14336, "
                         "M=1..64,128,256,512,1024,2048) + paged decode S=256 + causal prefill 8192",
             "M_sweep": list(I.M_SWEEP), "hidden": H, "N": list(Ns),
-            "gemm_tile": "one per-element chain (fp32 from 0, one v_mfma_f32_16x16x32_bf16 per 32-wide k chunk, ascending) dealt out by nine tiles chosen by shape, all bitwise equal: M<=64 (non-temporal weight loads): 64x64x128 where 64-wide tiles give >= 3/4 of the CUs in workgroups, else 16x16x256 (M<=16), 16x32x256 (M<=32) or 64x16x128 with 6 stages; M>64: the largest of 64x32x128 / 64x64x128 / 128x64x128 / 128x128x64 / 256x128x64 no taller than M rounded up to 64 giving >= 3/4 of the CUs in workgroups; global_load_lds pipelines of 3-6 stages, next k tile read from LDS during the current MFMAs",
+            "gemm_tile": "one per-element chain (fp32 from 0, one v_mfma_f32_16x16x32_bf16 per 32-wide k chunk, ascending) dealt out by nine tiles chosen by shape, all bitwise equal: M<=64 (non-temporal weight loads): 64x64x128 where 64-wide tiles give >= 3/4 of the CUs in workgroups, else 16x16x256 (M<=16), 16x32x256 (M<=32) or 32x32x128 with 6 stages; M>64: the largest of 64x32x128 / 64x64x128 / 128x64x128 / 128x128x64 / 256x128x64 no taller than M rounded up to 64 giving >= 3/4 of the CUs in workgroups; global_load_lds pipelines of 3-6 stages, next k tile read from LDS during the current MFMAs",
             "value_basis": "GEMM flops of the sweep / GPU time of the projection phase (HIP graph replay)",
             "graph_matches_eager": graph_matches_eager,
             "gpu_sclk_mhz_after_timed_steps": sclk_after,

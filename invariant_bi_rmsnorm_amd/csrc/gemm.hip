@@ -29,7 +29,7 @@
 //     weight loads are non-temporal.  When 64-wide n tiles still give three
 //     quarters of the CU count in workgroups, 64 x 64 x 128; otherwise narrow
 //     n tiles with deep k tiles, so that many weight bytes are in flight per
-//     CU: 16 x 16 x 256 (M <= 16), 16 x 32 x 256 (M <= 32), 64 x 16 x 128
+//     CU: 16 x 16 x 256 (M <= 16), 16 x 32 x 256 (M <= 32), 32 x 32 x 128
 //     with six stages (M <= 64).  (Cold weights, N = 4096, M <= 16: 8.5-8.9 us
 //     against 15.1-15.3 for the 64 x 32 x 128 tile; N = 14336: 22-26 us.)
 //   * M > 64: the largest of 64 x 32 x 128, 64 x 64 x 128, 128 x 64 x 128,

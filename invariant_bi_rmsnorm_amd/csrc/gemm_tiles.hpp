@@ -22,7 +22,7 @@ struct GemmTiles {
     using Qn = GemmTile<64, 64, 128, 2, 2, 3, kLib, 2>;
     using N16 = GemmTile<16, 16, 256, 1, 1, 4, kLib, 2>;
     using N32 = GemmTile<16, 32, 256, 1, 2, 4, kLib, 2>;
-    using N64 = GemmTile<64, 16, 128, 4, 1, 6, kLib, 2>;
+    using N64 = GemmTile<32, 32, 128, 2, 2, 6, kLib, 2>;     // M <= 64 in 32-row tiles
 };
 static_assert(std::is_same<GemmTiles<0>::M, BiTile>::value, "BiTile is the library's 128 x 64 x 128 tile");
 
