@@ -18,11 +18,12 @@ struct GemmTiles {
     using M = GemmTile<128, 64, 128, 4, 2, 3, kLib>;
     using L = GemmTile<128, 128, 64, 2, 4, 3, kLib>;
     using G = GemmTile<256, 128, 64, 4, 2, 3, kLib>;      // 8 wavefronts of 64 x 64
-    // small M: weights read non-temporally (each is read once per call)
+    // M <= 64: weights read non-temporally (each is read once per call);
+    // UpTo16/32/64 serve the M ranges where 64-wide tiles do not fill the CUs
     using Qn = GemmTile<64, 64, 128, 2, 2, 3, kLib, 2>;
-    using N16 = GemmTile<16, 16, 256, 1, 1, 4, kLib, 2>;
-    using N32 = GemmTile<16, 32, 256, 1, 2, 4, kLib, 2>;
-    using N64 = GemmTile<32, 32, 128, 2, 2, 6, kLib, 2>;     // M <= 64 in 32-row tiles
+    using UpTo16 = GemmTile<16, 16, 256, 1, 1, 4, kLib, 2>;
+    using UpTo32 = GemmTile<16, 32, 256, 1, 2, 4, kLib, 2>;
+    using UpTo64 = GemmTile<32, 32, 128, 2, 2, 6, kLib, 2>;
 };
 static_assert(std::is_same<GemmTiles<0>::M, BiTile>::value, "BiTile is the library's 128 x 64 x 128 tile");
 
@@ -46,7 +47,7 @@ int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const
 {
     using T = GemmTiles<kLib>;
     const int64_t need = (int64_t)device_cus() * 3 / 4;
-    int pick = 0;                                    // 0 S, 1 Q, 2 M, 3 L, 4 Qn, 5 N16, 6 N32, 7 N64, 8 G
+    int pick = 0;                                    // 0 S, 1 Q, 2 M, 3 L, 4 Qn, 5-7 UpTo16/32/64, 8 G
     if (M <= 64) {
         pick = (N + 63) / 64 >= need ? 4 : M <= 16 ? 5 : M <= 32 ? 6 : 7;
     } else {
@@ -61,9 +62,9 @@ int gemm_dispatch(const void* a, int64_t lda, const void* wt, int64_t ldw, const
     case 2: return gemm_launch<typename T::M>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     case 3: return gemm_launch<typename T::L>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     case 4: return gemm_launch<typename T::Qn>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 5: return gemm_launch<typename T::N16>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 6: return gemm_launch<typename T::N32>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
-    case 7: return gemm_launch<typename T::N64>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 5: return gemm_launch<typename T::UpTo16>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 6: return gemm_launch<typename T::UpTo32>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
+    case 7: return gemm_launch<typename T::UpTo64>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     case 8: return gemm_launch<typename T::G>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     default: return gemm_launch<typename T::S>(a, lda, wt, ldw, bias, c, ldc, c_dtype, M, N, K, stream);
     }
