@@ -19,22 +19,32 @@
 namespace {
 
 constexpr int kD = 128;
+constexpr int kThreads = 256;          // 32 lanes of 4 dims per head, 8 heads at a time
 
-__global__ __launch_bounds__(kD) void kv_append_kernel(
+// one workgroup per token: lane group tid/32 takes heads tid/32, tid/32 + 8, ...;
+// each lane moves 4 dims (8 bytes) of K and of V
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(
     const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn, int64_t ld,
     const int32_t* __restrict__ slots, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
     int64_t num_blocks, int Hkv)
 {
     const int64_t t = blockIdx.x;
-    const int h = blockIdx.y;
-    const int d = threadIdx.x;
     const int64_t slot = slots[t];
     if (slot < 0 || slot >= num_blocks * 16) return;
     const int64_t blk = slot >> 4;
     const int off = (int)(slot & 15);
-    const int64_t src = t * ld + (int64_t)h * kD + d;
-    kc[((blk * Hkv + h) * 16 + off) * kD + d] = kn[src];
-    vc[((blk * Hkv + h) * kD + d) * 16 + off] = vn[src];
+    const int d4 = (threadIdx.x & 31) * 4;
+    for (int h = threadIdx.x >> 5; h < Hkv; h += kThreads / 32) {
+        const int64_t src = t * ld + (int64_t)h * kD + d4;
+        const u32x2 kv = *reinterpret_cast<const u32x2*>(kn + src);
+        const u32x2 vv = *reinterpret_cast<const u32x2*>(vn + src);
+        *reinterpret_cast<u32x2*>(kc + ((blk * Hkv + h) * 16 + off) * kD + d4) = kv;
+        uint16_t* vd = vc + ((blk * Hkv + h) * kD + d4) * 16 + off;
+        vd[0] = (uint16_t)(vv[0] & 0xffffu);
+        vd[16] = (uint16_t)(vv[0] >> 16);
+        vd[32] = (uint16_t)(vv[1] & 0xffffu);
+        vd[48] = (uint16_t)(vv[1] >> 16);
+    }
 }
 
 }  // namespace
@@ -52,7 +62,7 @@ extern "C" int bi_kv_append(const void* k_new, const void* v_new, int64_t ld_new
         return BI_ERR_INVALID_ARGUMENT;
     if (D != kD || Hkv > 65535 || T > 0x7fffffffLL) return BI_ERR_UNSUPPORTED;
     if (T == 0) return BI_OK;
-    hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)T, Hkv), dim3(kD), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)T), dim3(kThreads), 0, (hipStream_t)stream,
                        (const uint16_t*)k_new, (const uint16_t*)v_new, ld_new, slots,
                        (uint16_t*)k_cache, (uint16_t*)v_cache, num_blocks, Hkv);
     return bi_launch_status();

@@ -45,9 +45,10 @@ def prefill(ops, cache, table, q_bits, q_start, kv_lens):
 
 # ------------------------------------------------------------------ append
 
-def test_kv_append_bitwise_layout(ops):
-    g = np.random.default_rng(1)
-    Hkv, T, nblk = 4, 50, 10
+@pytest.mark.parametrize("Hkv", [4, 12])
+def test_kv_append_bitwise_layout(ops, Hkv):
+    g = np.random.default_rng(Hkv)
+    T, nblk = 50, 10
     qkv = I.normal_bf16(g, (T, (16 + 2 * Hkv) * D))       # a fused projection output
     k = qkv[:, 16 * D:(16 + Hkv) * D].reshape(T, Hkv, D)
     v = qkv[:, (16 + Hkv) * D:].reshape(T, Hkv, D)
