@@ -118,7 +118,10 @@ size_t bi_toy_workspace_bytes(const bi_toy_config* cfg, int32_t max_tokens, int3
  * BI_ERR_WORKSPACE_TOO_SMALL when R rows do not fit the workspace.  Each row goes through the batch-invariant
  * kernels only, so next_ids[s] does not depend on which other sequences share
  * the step or on their order.  Requires head_dim == 128, hidden % 64 == 0,
- * mlp % 64 == 0 and the constraints of the bi.h entry points it calls. */
+ * mlp % 64 == 0 and the constraints of the bi.h entry points it calls.
+ * On return the workspace begins with the residual stream after the last
+ * layer: bf16 [T][hidden], row t for token t of the step (before the final
+ * RMSNorm), for callers that inspect or check intermediate states. */
 int bi_toy_step(const bi_toy_config* cfg, const bi_toy_weights* w, const bi_toy_step_desc* step,
                 void* ws, size_t ws_bytes, int32_t* next_ids, float* logits_out, void* stream);
 

@@ -39,7 +39,7 @@ Layout layout(const bi_toy_config* c, int64_t T, int64_t S, int32_t max_kv_len)
     const size_t QKV = (Hq + 2 * Hkv) * D;
     Layout L{};
     size_t o = 0;
-    L.h = o;      o += up((size_t)T * H * 2);
+    L.h = o;      o += up((size_t)T * H * 2);   // first: the residual stream, left in place on return
     L.xn = o;     o += up((size_t)T * H * 2);
     L.qkv = o;    o += up((size_t)T * QKV * 2);
     L.attn = o;   o += up((size_t)T * Hq * D * 2);

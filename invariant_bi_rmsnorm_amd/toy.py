@@ -152,6 +152,13 @@ class ToyEngine:
         self.free.extend(r.blocks)
         r.blocks = []
 
+    def hidden_states(self, T: int) -> torch.Tensor:
+        """The residual stream after the last layer of the latest step: bf16
+        [T, hidden] at the start of the workspace, row t for token t of the
+        step (include/bi_toy.h); a view, overwritten by the next step."""
+        H = self.cfg["hidden"]
+        return self.ws[:T * H * 2].view(torch.bfloat16).view(T, H)
+
     # ---------------------------------------------------------------- one step
     def step(self, work, want_logits: bool = False, temperature: float = 0.0, all_rows=(),
              fp32_head_margin: float = 0.0):

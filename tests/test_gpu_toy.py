@@ -12,7 +12,7 @@ import time
 import numpy as np
 import pytest
 
-from gpu_util import check_bf16, dev_bf16, dev_i32, host_bits, log
+from gpu_util import bf16_f64, check_bf16, dev_bf16, dev_i32, host_bits, log
 from test_toy_tolerance import TOY_MAX_BAR, TOY_RMS_BAR
 from invariant_bi_rmsnorm_amd import inputs as I
 
@@ -149,6 +149,55 @@ def test_toy_logits_parity_at_each_depth(ops, orc, toy_weights, layers):
     top2 = np.sort(ref)[-2:]
     if top2[1] - top2[0] > 2 * err.max():
         assert int(nxt[0]) == int(np.argmax(ref))
+
+
+def test_toy_each_layer_from_gpu_input_bits_matches_the_oracle_layer(ops, orc, toy_weights):
+    """Each of the 8 layers alone: the driver's residual stream after layer l
+    (the model cut after l layers, 64-token prompt) against the oracle's layer
+    l applied to the GPU's own stream after layer l - 1 (the embedding rows for
+    l = 1).  No rounding difference carries over from earlier layers, so each
+    layer's wiring (QKV slicing, RoPE of q and k, GQA grouping, gate|up split,
+    residual adds) is pinned on its own; a wiring slip moves the stream by a
+    sizeable part of a branch's RMS.
+
+    The bar is set, as for the depth test, by how far an independent CPU
+    evaluation of the same layer from the same input bits drifts from the
+    oracle: error RMS within 1.6x and max error within 2x of that drift.  The
+    CPU evaluation (fp32, each op rounded to bf16) rounds the softmax weights
+    to bf16 before their sum and the value product, as the kernels' attention
+    splits do.  That rounding dominates the drift of the stream: without it the
+    fp32 evaluation leaves 10% of the stream values off the oracle's by an ulp
+    at the first layer, with it 43%, as many as the GPU.  The per-op bar (1e-2
+    of the output's RMS) is not used here: a layer chains about ten rounded
+    ops, and even that CPU evaluation exceeds the per-op bar on each half of
+    the layer (up to 2.8x on the attention half)."""
+    import toy_layer_oracle as TL
+    from invariant_bi_rmsnorm_amd.toy import Request
+    from toy_ref32 import layer_fp32
+    prompt = I.toy_prompt(I.TOY, 64)
+    T = len(prompt)
+    prev = np.ascontiguousarray(toy_weights["embed"][prompt])
+    for l in range(1, I.TOY["layers"] + 1):
+        cfg = dict(I.TOY, layers=l)
+        w = dict(toy_weights, layers=toy_weights["layers"][:l])
+        eng = make_engine(w, cfg=cfg, num_blocks=64, max_tokens=T, max_seqs=1, max_kv_len=T)
+        eng.step([(Request(0, prompt, 1), T)])
+        got = host_bits(eng.hidden_states(T))
+        del eng
+        lw = toy_weights["layers"][l - 1]
+        ref = TL.layer(orc, I.TOY, lw, prev)
+        alt = layer_fp32(I.TOY, lw, prev, bf16_weights=True)
+        r64 = bf16_f64(ref)
+        rms = math.sqrt(float(np.mean(r64 ** 2)))
+        drift = np.abs(bf16_f64(alt) - r64)
+        err = np.abs(bf16_f64(got) - r64)
+        d_rms, e_rms = math.sqrt(float(np.mean(drift ** 2))), math.sqrt(float(np.mean(err ** 2)))
+        log(f"layer {l}: gpu rms err {e_rms / rms:.3e}, max {err.max() / rms:.3e} of RMS; CPU evaluation "
+            f"{d_rms / rms:.3e}, {drift.max() / rms:.3e}; bit-equal to the oracle: gpu "
+            f"{np.mean(got == ref):.3f}, CPU evaluation {np.mean(alt == ref):.3f}")
+        assert e_rms <= DEPTH_RMS_RATIO * d_rms, f"layer {l}"
+        assert err.max() <= DEPTH_MAX_RATIO * drift.max(), f"layer {l}"
+        prev = got
 
 
 def test_toy_verify_step_logit_rows_match_the_oracle(ops, orc, toy_weights):

@@ -19,10 +19,8 @@ def _r16(x):
     return I.f32_to_bf16(np.asarray(x, np.float32))
 
 
-def toy_logits_fp32(cfg: dict, w: dict, ids) -> np.ndarray:
-    T = len(ids)
-    H, D, Hq, Hkv, F = cfg["hidden"], cfg["head_dim"], cfg["heads"], cfg["kv_heads"], cfg["mlp"]
-    G = Hq // Hkv
+def _ops(cfg: dict):
+    D = cfg["head_dim"]
     eps = np.float32(cfg["eps"])
 
     def rms(x, wt):
@@ -43,28 +41,50 @@ def toy_logits_fp32(cfg: dict, w: dict, ids) -> np.ndarray:
         a, b = xf[..., :half], xf[..., half:]
         return _r16(np.concatenate([a * c - b * s, b * c + a * s], -1))
 
+    return rms, mm, rope
+
+
+def layer_fp32(cfg: dict, lw: dict, h, bf16_weights: bool = False) -> np.ndarray:
+    """One decoder layer in fp32 over the T tokens of one prompt (positions
+    0..T-1): h [T, hidden] bf16 bits -> the residual stream after it (bf16 bits).
+    bf16_weights: the softmax weights exp(s - max) are rounded to bf16 before
+    their sum and the value product, the weights' rounding the library's
+    attention splits apply (prompts of at most 256 tokens are one split)."""
+    T = h.shape[0]
+    D, Hq, Hkv, F = cfg["head_dim"], cfg["heads"], cfg["kv_heads"], cfg["mlp"]
+    G = Hq // Hkv
+    rms, mm, rope = _ops(cfg)
     pos = np.arange(T)
-    h = w["embed"][np.asarray(ids)]
     causal = np.tril(np.ones((T, T), bool))
-    for lw in w["layers"]:
-        xn = rms(h, lw["attn_norm"])
-        qkv = mm(xn, lw["wqkv"]).reshape(T, Hq + 2 * Hkv, D)
-        q = rope(qkv[:, :Hq], pos)
-        k = rope(qkv[:, Hq:Hq + Hkv], pos)
-        v = qkv[:, Hq + Hkv:]
-        out = np.zeros((T, Hq, D), np.float32)
-        for hh in range(Hq):
-            s = (_f(q[:, hh]) @ _f(k[:, hh // G]).T) / np.float32(math.sqrt(D))
-            s = np.where(causal, s, -np.inf)
-            p = np.exp(s - s.max(-1, keepdims=True))
+    xn = rms(h, lw["attn_norm"])
+    qkv = mm(xn, lw["wqkv"]).reshape(T, Hq + 2 * Hkv, D)
+    q = rope(qkv[:, :Hq], pos)
+    k = rope(qkv[:, Hq:Hq + Hkv], pos)
+    v = qkv[:, Hq + Hkv:]
+    out = np.zeros((T, Hq, D), np.float32)
+    for hh in range(Hq):
+        s = (_f(q[:, hh]) @ _f(k[:, hh // G]).T) / np.float32(math.sqrt(D))
+        s = np.where(causal, s, -np.inf)
+        p = np.exp(s - s.max(-1, keepdims=True))
+        if bf16_weights:
+            p = _f(_r16(p))
+            out[:, hh] = (p @ _f(v[:, hh // G])) / p.sum(-1, keepdims=True)
+        else:
             p /= p.sum(-1, keepdims=True)
             out[:, hh] = p @ _f(v[:, hh // G])
-        o = mm(_r16(out).reshape(T, -1), lw["wo"])
-        h = _r16(_f(h) + _f(o))
-        xn = rms(h, lw["mlp_norm"])
-        gu = _f(mm(xn, lw["wgu"]))
-        g, u = gu[:, :F], gu[:, F:]
-        d = mm(_r16(g / (1 + np.exp(-g)) * u), lw["wd"])
-        h = _r16(_f(h) + _f(d))
+    o = mm(_r16(out).reshape(T, -1), lw["wo"])
+    h = _r16(_f(h) + _f(o))
+    xn = rms(h, lw["mlp_norm"])
+    gu = _f(mm(xn, lw["wgu"]))
+    g, u = gu[:, :F], gu[:, F:]
+    d = mm(_r16(g / (1 + np.exp(-g)) * u), lw["wd"])
+    return _r16(_f(h) + _f(d))
+
+
+def toy_logits_fp32(cfg: dict, w: dict, ids) -> np.ndarray:
+    rms, _, _ = _ops(cfg)
+    h = w["embed"][np.asarray(ids)]
+    for lw in w["layers"]:
+        h = layer_fp32(cfg, lw, h)
     xn = rms(h[-1:], w["final_norm"])
     return (_f(xn) @ _f(w["lm_head"]).astype(np.float32).T)[0].astype(np.float64)
