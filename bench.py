@@ -594,7 +594,53 @@ def main():
     result["copy_probe"] = {"bytes_read": COPY_PROBE_BYTES, "bytes_written": COPY_PROBE_BYTES,
                             "us": round(copy_us, 1),
                             "GB/s": round(2 * COPY_PROBE_BYTES / (copy_us * 1e-6) / 1e9, 1)}
-    del src, dst
+    # read probe: the achievable HBM read rate (the buffer is twice the
+    # last-level cache), the practical ceiling of decode and of the GEMMs that
+    # stream their weights
+    sink = torch.zeros(ops.PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+    ops.bi_probe_read(src, sink)
+    torch.cuda.synchronize()
+    cs, ce = E(), E()
+    cs.record(stream)
+    for _ in range(5):
+        ops.bi_probe_read(src, sink)
+    ce.record(stream)
+    torch.cuda.synchronize()
+    read_us = cs.elapsed_time(ce) * 1e3 / 5
+    read_gbs = COPY_PROBE_BYTES / (read_us * 1e-6) / 1e9
+    result["read_probe"] = {"bytes": COPY_PROBE_BYTES, "us": round(read_us, 1), "GB/s": round(read_gbs, 1),
+                            "frac_hbm": round(read_gbs / PEAK_HBM_GBS, 4)}
+    # global -> LDS fill rate of the staging instruction, by where the data
+    # comes from (L2 of each XCD, last-level cache, HBM), one and two
+    # workgroups of 8 wavefronts per CU: the feed rate that bounds the GEMM
+    # tiles, which stage (BM + BN) x BK x 2 bytes per k tile
+    clk_mhz = sclk_after or 2400
+    fill = []
+    for span in (2 << 20, 64 << 20, COPY_PROBE_BYTES):
+        for per_cu in (1, 2):
+            wgs = 256 * per_cu
+            iters = (16 << 20) // (8 * 8192) // per_cu
+            ops.bi_probe_lds_fill(src, span, wgs, iters, sink)
+            torch.cuda.synchronize()
+            cs, ce = E(), E()
+            cs.record(stream)
+            for _ in range(3):
+                ops.bi_probe_lds_fill(src, span, wgs, iters, sink)
+            ce.record(stream)
+            torch.cuda.synchronize()
+            us = cs.elapsed_time(ce) * 1e3 / 3
+            moved = wgs * 8 * iters * 8192
+            fill.append({"span_MB": span >> 20, "workgroups_per_CU": per_cu, "us": round(us, 1),
+                         "TB/s": round(moved / (us * 1e-6) / 1e12, 2),
+                         "B_per_clk_per_CU": round(moved / (us * 1e-6) / (clk_mhz * 1e6) / 256, 1)})
+    result["lds_fill_probe"] = {"rows": fill, "clock_MHz": clk_mhz,
+                                "note": "global_load_lds_dwordx4, 8 wavefronts per workgroup, 8-16 1 KB "
+                                        "loads in flight per wavefront; 256 CUs"}
+    result["roofline"]["achievable_read_GB/s"] = round(read_gbs, 1)
+    result["roofline"]["frac_of_achievable_read"] = round(result["roofline"]["achieved"] / read_gbs, 4)
+    if "decode_attn" in result:
+        result["decode_attn"]["frac_of_read_probe"] = round(result["decode_attn"]["GB/s"] / read_gbs, 4)
+    del src, dst, sink
 
     # the same sweep of GEMMs (no RMSNorm) through the invariant library and through
     # libbi_nb.so (batch-size-dependent K order at small M), each as a HIP graph

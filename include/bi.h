@@ -338,6 +338,37 @@ int bi_probe_mfma_bf16(const void* a, const void* b, float* c, void* stream);
  */
 int bi_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/* Words of the sink array the two probes below write (device uint32). */
+#define BI_PROBE_SINK_WORDS 8192
+
+/*
+ * Diagnostic: reads src[0:bytes] once with a plain streaming kernel (each
+ * wavefront reads whole 8 KB blocks, eight 16-byte loads per lane in flight,
+ * up to 16 wavefronts per CU): the achievable HBM read
+ * bandwidth, the ceiling of the weight-streaming GEMMs and of decode, which
+ * read far more than they write.  Each wavefront writes the xor of the 32-bit
+ * words it read to one word of sink (device uint32 [BI_PROBE_SINK_WORDS]), so
+ * the xor of all sink words equals the xor of all words of src (words the
+ * call does not use keep their contents).  bytes % 16 == 0, 16-byte aligned
+ * src.
+ */
+int bi_probe_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
+/*
+ * Diagnostic: the global -> LDS fill rate of global_load_lds_dwordx4, the
+ * instruction the GEMM and attention kernels stage their operands with.
+ * `workgroups` workgroups of 8 wavefronts each move iters x 8 KB per
+ * wavefront from src into LDS (1 KB per load, 8 to 16 loads in flight per
+ * wavefront), reading the first span_bytes of src over and over: a span of a
+ * few MB is served by each XCD's L2, tens of MB by the last-level cache, a GB
+ * by HBM.  Total bytes moved: workgroups * 8 * iters * 8192.  sink (device
+ * uint32 [BI_PROBE_SINK_WORDS]) receives one word per workgroup.
+ * span_bytes % 1024 == 0 and >= 1024, 1 <= workgroups <= BI_PROBE_SINK_WORDS,
+ * iters >= 1, 16-byte aligned src of at least span_bytes.
+ */
+int bi_probe_lds_fill(const void* src, int64_t span_bytes, int32_t workgroups, int32_t iters, uint32_t* sink,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

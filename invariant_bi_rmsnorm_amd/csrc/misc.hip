@@ -42,6 +42,62 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
     for (; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Plain streaming read: wavefront w of the grid reads the 8 KB blocks w,
+// w + W, w + 2W, ... (W wavefronts in all), eight 16-byte loads per lane in
+// flight, each covering 1 KB of the block: the achievable HBM read bandwidth.
+// Each wavefront writes the xor of every 32-bit word it read to sink[w], so
+// no load is dead and the sink words xor to the xor of the whole buffer.
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                   uint32_t* __restrict__ sink)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t W = (int64_t)gridDim.x * 4;
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    uint32_t acc = 0;
+    for (int64_t b = w; b * 512 < n16; b += W) {          // 512 16-byte units per block
+        u32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t i = b * 512 + 64 * j + lane;
+            v[j] = i < n16 ? src[i] : zero_u32x4();
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+    }
+    for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+    if (lane == 0) sink[w] = acc;
+}
+
+// Global -> LDS fill rate: each of the 8 wavefronts of a workgroup streams
+// iters x 8 KB from src (1 KB global_load_lds_dwordx4 loads, the GEMM and
+// attention kernels' staging instruction; 8 to 16 in flight per wavefront)
+// into its own 8 KB of LDS, wrapping inside the first span_chunks KB of src.
+// The span decides where the data comes from: a few MB stay in each XCD's L2,
+// tens of MB in the last-level cache, a GB in HBM.
+constexpr int kFillWaves = 8;
+__global__ __launch_bounds__(64 * kFillWaves) void lds_fill_kernel(const uint16_t* __restrict__ src,
+                                                                   int64_t span_chunks, int iters,
+                                                                   uint32_t* __restrict__ sink)
+{
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kFillWaves * 8 * 512];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int64_t chunk = ((int64_t)blockIdx.x * kFillWaves + wave) * 8;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t c = (chunk + j) % span_chunks;
+            __builtin_amdgcn_global_load_lds(src + c * 512 + lane * 8, lds + (wave * 8 + j) * 512, 16, 0, 0);
+        }
+        // at most the 8 loads just issued stay in flight (vmcnt 8; lgkmcnt, expcnt unconstrained)
+        __builtin_amdgcn_s_waitcnt((8 & 0xF) | (0x7 << 4) | (0xF << 8));
+        chunk += (int64_t)gridDim.x * kFillWaves * 8;
+    }
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));   // vmcnt 0: every load has landed
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = lds[lane];
+}
+
 }  // namespace
 
 extern "C" int bi_abi_version(void) { return BI_ABI_VERSION; }
@@ -82,6 +138,37 @@ extern "C" int bi_probe_copy(const void* src, void* dst, int64_t bytes, void* st
     const unsigned grid = (unsigned)(want < 256 * 16 ? want : 256 * 16);
     hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src,
                        (u32x4*)dst, n16);
+    return bi_launch_status();
+    BI_TRY_END
+}
+
+extern "C" int bi_probe_read(const void* src, int64_t bytes, uint32_t* sink, void* stream)
+{
+    BI_TRY_BEGIN
+    if (bytes < 0 || (bytes % 16)) return BI_ERR_INVALID_ARGUMENT;
+    if (bytes > 0 && (!src || !sink || !bi_aligned(src, 16) || !bi_aligned(sink, 4)))
+        return BI_ERR_INVALID_ARGUMENT;
+    if (bytes == 0) return BI_OK;
+    const int64_t n16 = bytes / 16;
+    const int64_t blocks = (n16 + 511) / 512;                  // 8 KB blocks, 4 wavefronts per workgroup
+    const int64_t want = (blocks + 3) / 4;
+    const unsigned grid = (unsigned)(want < 1024 ? want : 1024);   // 16 wavefronts per CU at most
+    hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, n16,
+                       sink);
+    return bi_launch_status();
+    BI_TRY_END
+}
+
+extern "C" int bi_probe_lds_fill(const void* src, int64_t span_bytes, int32_t workgroups, int32_t iters,
+                                 uint32_t* sink, void* stream)
+{
+    BI_TRY_BEGIN
+    if (!src || !sink || !bi_aligned(src, 16) || !bi_aligned(sink, 4)) return BI_ERR_INVALID_ARGUMENT;
+    if (span_bytes < 1024 || (span_bytes % 1024) || workgroups <= 0 || workgroups > BI_PROBE_SINK_WORDS ||
+        iters <= 0)
+        return BI_ERR_INVALID_ARGUMENT;
+    hipLaunchKernelGGL(lds_fill_kernel, dim3(workgroups), dim3(64 * kFillWaves), 0, (hipStream_t)stream,
+                       (const uint16_t*)src, span_bytes / 1024, iters, sink);
     return bi_launch_status();
     BI_TRY_END
 }

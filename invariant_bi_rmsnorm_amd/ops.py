@@ -60,6 +60,8 @@ SIGNATURES = {
     "bi_lm_head_f32": (ctypes.c_int, [_P, _I64, _P, _F, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _F, _P]),
     "bi_probe_mfma_bf16": (ctypes.c_int, [_P, _P, _P, _P]),
     "bi_probe_copy": (ctypes.c_int, [_P, _P, _I64, _P]),
+    "bi_probe_read": (ctypes.c_int, [_P, _I64, _P, _P]),
+    "bi_probe_lds_fill": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P]),
     # include/bi_toy.h
     "bi_embed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "bi_rope_table": (ctypes.c_int, [_P, _I32, _I32, ctypes.c_double, _P]),
@@ -461,6 +463,42 @@ def bi_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst too small")
     _check(lib().bi_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "bi_probe_copy")
+
+
+# words of the probes' sink array (BI_PROBE_SINK_WORDS in include/bi.h)
+PROBE_SINK_WORDS = 8192
+
+
+def _probe_sink(sink: Optional[torch.Tensor], device) -> torch.Tensor:
+    if sink is None:
+        return torch.zeros(PROBE_SINK_WORDS, dtype=torch.int32, device=device)
+    _need_dense(sink, torch.int32, (PROBE_SINK_WORDS,), "sink")
+    return sink
+
+
+def bi_probe_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Streams src once (achievable HBM read rate); returns the sink words,
+    whose xor is the xor of src's 32-bit words (words past the grid stay 0)."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    sink = _probe_sink(sink, src.device)
+    _check(lib().bi_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
+           "bi_probe_read")
+    return sink
+
+
+def bi_probe_lds_fill(src: torch.Tensor, span_bytes: int, workgroups: int, iters: int,
+                      sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Global -> LDS fill of workgroups * 8 * iters * 8 KB from the first
+    span_bytes of src (include/bi.h)."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    if span_bytes > src.numel() * src.element_size():
+        raise ValueError("span beyond src")
+    sink = _probe_sink(sink, src.device)
+    _check(lib().bi_probe_lds_fill(_ptr(src), int(span_bytes), int(workgroups), int(iters), _ptr(sink),
+                                   _stream(stream)), "bi_probe_lds_fill")
+    return sink
 
 
 def bi_probe_mfma_bf16(a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:

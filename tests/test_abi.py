@@ -193,6 +193,21 @@ def test_probe_copy_validation(L):
     assert L.bi_probe_copy(MIS, A16, 32, None) == 1
 
 
+def test_probe_read_and_lds_fill_validation(L):
+    assert L.bi_probe_read(A16, 0, A16, None) == 0
+    assert L.bi_probe_read(A16, 17, A16, None) == 1
+    assert L.bi_probe_read(MIS, 32, A16, None) == 1
+    assert L.bi_probe_read(A16, 32, None, None) == 1
+    f = L.bi_probe_lds_fill
+    assert f(A16, 1000, 1, 1, A16, None) == 1          # span not a whole number of KB
+    assert f(A16, 0, 1, 1, A16, None) == 1
+    assert f(A16, 1024, 0, 1, A16, None) == 1
+    assert f(A16, 1024, 8193, 1, A16, None) == 1        # more workgroups than sink words
+    assert f(A16, 1024, 1, 0, A16, None) == 1
+    assert f(MIS, 1024, 1, 1, A16, None) == 1
+    assert f(A16, 1024, 1, 1, None, None) == 1
+
+
 def test_argmax_validation(L):
     f = L.bi_argmax
     assert f(A16, 100, 0, 100, A16, None) == 0

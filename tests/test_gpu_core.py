@@ -58,6 +58,27 @@ def test_mfma_result_independent_of_row_and_column_position(ops):
         assert np.array_equal(c2[3].view(np.uint32), c0[3].view(np.uint32))
 
 
+def test_probe_read_sees_every_word_once(ops):
+    """The read probe's sink words xor to the xor of the buffer's 32-bit words
+    (each word read exactly once), at a size with a grid-stride tail."""
+    g = np.random.default_rng(11)
+    for n in (4, 4096 * 4 + 12, 3_000_000):
+        log(f"probe read: {n} words")
+        words = g.integers(0, 2 ** 32, size=n, dtype=np.uint64).astype(np.uint32)
+        src = torch.from_numpy(words.view(np.int32)).cuda()
+        sink = ops.bi_probe_read(src)
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(words)
+
+
+def test_probe_lds_fill_runs(ops):
+    src = torch.zeros(1 << 20, dtype=torch.int16, device="cuda") + 7
+    log("probe lds fill")
+    sink = ops.bi_probe_lds_fill(src, 1 << 20, 256, 4)
+    torch.cuda.synchronize()
+    assert np.all(sink[:256].cpu().numpy() == 7)
+
+
 # ------------------------------------------------------------------ RMSNorm
 
 def test_rmsnorm_tiny_parity_and_invariance(ops, orc):
