@@ -40,7 +40,7 @@ M_SWEEP = list(range(1, 65)) + [128, 256, 512, 1024, 2048]
 
 KERNELS = ("gemm_kernel", "rmsnorm_kernel", "decode_split_kernel", "decode_combine_kernel",
            "decode_ticket_reset", "prefill_kernel", "kv_append_kernel", "copy_kernel", "log_softmax_kernel",
-           "nb_splitk_reduce")
+           "nb_splitk_reduce", "read_kernel", "lds_fill_kernel")
 
 
 def src_hash(*names):
