@@ -614,7 +614,6 @@ def main():
     # comes from (L2 of each XCD, last-level cache, HBM), one and two
     # workgroups of 8 wavefronts per CU: the feed rate that bounds the GEMM
     # tiles, which stage (BM + BN) x BK x 2 bytes per k tile
-    clk_mhz = sclk_after or 2400
     fill = []
     for span in (2 << 20, 64 << 20, COPY_PROBE_BYTES):
         for per_cu in (1, 2):
@@ -629,11 +628,18 @@ def main():
             ce.record(stream)
             torch.cuda.synchronize()
             us = cs.elapsed_time(ce) * 1e3 / 3
-            moved = wgs * 8 * iters * 8192
             fill.append({"span_MB": span >> 20, "workgroups_per_CU": per_cu, "us": round(us, 1),
-                         "TB/s": round(moved / (us * 1e-6) / 1e12, 2),
-                         "B_per_clk_per_CU": round(moved / (us * 1e-6) / (clk_mhz * 1e6) / 256, 1)})
+                         "bytes": wgs * 8 * iters * 8192})
+    # per clock at the shader clock read right after the probe (2400 MHz, the
+    # nominal peak clock, when the box does not expose it)
+    sclk_probe = gpu_sclk_mhz()
+    clk_mhz = sclk_probe if isinstance(sclk_probe, int) else 2400
+    for r in fill:
+        moved = r.pop("bytes")
+        r["TB/s"] = round(moved / (r["us"] * 1e-6) / 1e12, 2)
+        r["B_per_clk_per_CU"] = round(moved / (r["us"] * 1e-6) / (clk_mhz * 1e6) / 256, 1)
     result["lds_fill_probe"] = {"rows": fill, "clock_MHz": clk_mhz,
+                                "clock_source": "sysfs" if isinstance(sclk_probe, int) else "nominal",
                                 "note": "global_load_lds_dwordx4, 8 wavefronts per workgroup, 8-16 1 KB "
                                         "loads in flight per wavefront; 256 CUs"}
     result["roofline"]["achievable_read_GB/s"] = round(read_gbs, 1)
