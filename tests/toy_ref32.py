@@ -81,10 +81,10 @@ def layer_fp32(cfg: dict, lw: dict, h, bf16_weights: bool = False) -> np.ndarray
     return _r16(_f(h) + _f(d))
 
 
-def toy_logits_fp32(cfg: dict, w: dict, ids) -> np.ndarray:
+def toy_logits_fp32(cfg: dict, w: dict, ids, bf16_weights: bool = False) -> np.ndarray:
     rms, _, _ = _ops(cfg)
     h = w["embed"][np.asarray(ids)]
     for lw in w["layers"]:
-        h = layer_fp32(cfg, lw, h)
+        h = layer_fp32(cfg, lw, h, bf16_weights)
     xn = rms(h[-1:], w["final_norm"])
     return (_f(xn) @ _f(w["lm_head"]).astype(np.float32).T)[0].astype(np.float64)
