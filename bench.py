@@ -146,6 +146,34 @@ def traffic_from_profile():
     return d.get("traffic_bytes_per_launch")
 
 
+def invariance_cost(result: dict) -> dict:
+    """Time of the invariant build over the time of the same work through the
+    non-invariant baseline library (libbi_nb.so), per phase, from the rows the
+    run measured (above 1: invariance costs time).  The pages price it at
+    about 20% for the matmul alone and 42 s against 26 s end to end."""
+    out = {}
+    nb = result.get("baseline_nb_gemm_sweep", {})
+    if "nb_TFLOP/s" in nb:
+        out["gemm_sweep"] = round(nb["nb_TFLOP/s"] / nb["invariant_TFLOP/s"], 3)
+    sup = result.get("supplementary", {})
+    for r in sup.get("decode_S_sweep", {}).get("rows", []):
+        if r["S"] == 256 and r.get("nb_us"):
+            out["decode_S256"] = round(r["us"] / r["nb_us"], 3)
+    for r in sup.get("prefill_P_sweep", {}).get("rows", []):
+        if r.get("nb_us"):
+            key = f"prefill_P{r['P']}" + (f"_chunks{r['chunks']}" if "chunks" in r else "")
+            out[key] = round(r["us"] / r["nb_us"], 3)
+    toy = result.get("toy_experiment", {})
+    if "invariant_over_nb_time" in toy:
+        out["toy_100_runs"] = toy["invariant_over_nb_time"]
+        out["toy_unique_completions"] = {"invariant": toy["invariant"]["unique_completions"],
+                                         "nb": toy["nb"]["unique_completions"]}
+    out["note"] = ("invariant time / libbi_nb.so time for the same work, from the rows above; the pages: "
+                   "about 20% for the matmul alone, 26 s (default) against 55 s and then 42 s (invariant) end "
+                   "to end")
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -850,6 +878,7 @@ def main():
         except Exception as e:  # context only: never lose the result line for it
             beside["error"] = f"{type(e).__name__}: {e}"[:300]
         result["cpu_oracle_beside"] = beside
+    result["invariance_cost"] = invariance_cost(result)
     print(json.dumps(result), flush=True)
 
 

@@ -112,3 +112,22 @@ def test_profile_summary_names_kernels_by_library():
     assert short("decode_split_kernel(int, float)") == "decode_split_kernel"
     assert short("void (anonymous namespace)::rmsnorm_kernel<0>(unsigned short const*)") == "rmsnorm_kernel"
     assert short("void at::native::vectorized_elementwise_kernel<4>(int)").startswith("void at::native")
+
+
+def test_invariance_cost_is_invariant_over_baseline_time_per_phase():
+    b = _load_bench()
+    result = {
+        "baseline_nb_gemm_sweep": {"invariant_TFLOP/s": 300.0, "nb_TFLOP/s": 270.0},
+        "supplementary": {
+            "decode_S_sweep": {"rows": [{"S": 128, "us": 9.0, "nb_us": 8.0}, {"S": 256, "us": 520.0, "nb_us": 500.0}]},
+            "prefill_P_sweep": {"rows": [{"P": 8192, "us": 800.0, "nb_us": 800.0},
+                                         {"P": 8192, "chunks": 2000, "us": 1100.0, "nb_us": 1210.0}]}},
+        "toy_experiment": {"invariant_over_nb_time": 0.98, "invariant": {"unique_completions": 1},
+                           "nb": {"unique_completions": 63}},
+    }
+    c = b.invariance_cost(result)
+    assert c["gemm_sweep"] == 0.9                    # time ratio = inverse of the throughput ratio
+    assert c["decode_S256"] == 1.04 and "decode_S128" not in c
+    assert c["prefill_P8192"] == 1.0 and c["prefill_P8192_chunks2000"] == 0.909
+    assert c["toy_100_runs"] == 0.98 and c["toy_unique_completions"] == {"invariant": 1, "nb": 63}
+    assert set(b.invariance_cost({})) == {"note"}     # phases not run leave no entry
