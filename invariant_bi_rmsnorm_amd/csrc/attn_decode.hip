@@ -7,7 +7,8 @@
 // the length mix or the number of sequences.
 //
 // Three kernels:
-//  0. decode_ticket_reset zeroes the work counter at the head of the workspace.
+//  0. decode_ticket_reset zeroes the work counter at the head of the workspace
+//     and writes the zero output of sequences with no token.
 //  1. decode_split_kernel: persistent workgroups (as many as fit on the GPU at
 //     once) over the work list of (sequence, split, KV head) items.  Each
 //     workgroup first builds the prefix of split counts ceil(kv_len/256) of
@@ -25,7 +26,8 @@
 //     the values chain of the whole split for 32 of the 128 head dims.  The
 //     split's (m, l, o[128]) is written, fp32, to the workspace.
 //  2. decode_combine_kernel: per (sequence, query head), fold the splits in
-//     ascending order and divide.
+//     ascending order and divide; not launched when max_kv_len <= 256 (every
+//     sequence is one split, finished by the split kernel).
 // All arithmetic goes through attn_core.hpp, shared with the prefill kernel,
 // which is why decode at length L equals prefill row L-1 bit for bit.
 #include <mutex>

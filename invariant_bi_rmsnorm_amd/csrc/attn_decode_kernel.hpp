@@ -471,12 +471,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     *reinterpret_cast<u32x4*>(st_p) = st_v;
 }
 
-// Zeroes the split kernel's ticket counter (a kernel rather than a memset, so
-// the launch sequence can be captured in a HIP graph and replayed).
+// Runs before the split kernel: zeroes its ticket counter (a kernel rather
+// than a memset, so the launch sequence can be captured in a HIP graph and
+// replayed), and writes the zero output of every sequence with no token
+// (kv_len <= 0), which no split covers.  Wavefront w of the grid takes
+// sequence w; 256 threads per workgroup.
 constexpr size_t kTicketBytes = 256;
-__global__ void decode_ticket_reset(unsigned* tickets)
+__global__ __launch_bounds__(256) void decode_ticket_reset(unsigned* __restrict__ tickets,
+                                                           const int32_t* __restrict__ kv_lens, int cap, int S,
+                                                           int Hq, uint16_t* __restrict__ out, int64_t ldo)
 {
-    if (threadIdx.x == 0) *tickets = 0u;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tickets = 0u;
+    const int s = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (s >= S || clamp_len(kv_lens[s], cap) != 0) return;      // wave-uniform
+    const int lane = threadIdx.x & 63;
+    uint16_t* row = out + (int64_t)s * ldo;              // out is only 2-byte aligned
+    for (int e = lane; e < Hq * kD; e += 64) row[e] = 0;
 }
 
 // Fold of the split partials of one (sequence, query head), 128 threads (one
@@ -508,11 +518,7 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
     const int L = clamp_len(kv_lens[s], cap);
     const int n = (L + split_len - 1) / split_len;
     uint16_t* o = out + (int64_t)s * ldo + (int64_t)h * kD + d;
-    if (n == 0) {
-        *o = 0;
-        return;
-    }
-    if (n == 1) return;            // written by the split kernel
+    if (n <= 1) return;            // written by the split kernel (n = 1) or decode_ticket_reset (n = 0)
     const int G = Hq / Hkv;
     const int g = h / G;
     const float* base = ws_o + ((int64_t)s * Hq + h) * max_splits * kD;
@@ -669,7 +675,9 @@ static inline int decode_launch(const void* q, int64_t ldq, const void* k_cache,
     const float scale_log2 = scale_log2_of(scale);
     hipStream_t st = (hipStream_t)stream;
     const DecodeWs w = decode_ws_layout(ws, S, Hq, max_splits);
-    hipLaunchKernelGGL(decode_ticket_reset, dim3(1), dim3(64), 0, st, w.tickets);
+    const int cap = std::min(max_blocks * kBlock, max_splits * split_len);
+    hipLaunchKernelGGL(decode_ticket_reset, dim3((S + 3) / 4), dim3(256), 0, st, w.tickets, kv_lens, cap, S, Hq,
+                       (uint16_t*)out, ldo);
     int rc = bi_launch_status();
     if (rc != BI_OK) return rc;
     hipLaunchKernelGGL(decode_split_kernel, dim3(P), dim3(kThreads), 0, st,
@@ -678,9 +686,10 @@ static inline int decode_launch(const void* q, int64_t ldq, const void* k_cache,
                        scale_log2, w.o, w.ml, (uint16_t*)out, ldo, w.tickets);
     rc = bi_launch_status();
     if (rc != BI_OK) return rc;
+    // every sequence fits one split: the split kernel has written all outputs
+    if (max_splits == 1) return BI_OK;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(Hq, S), dim3(kD), 0, st, (const float*)w.o,
-                       (const float*)w.ml, kv_lens, std::min(max_blocks * kBlock, max_splits * split_len), Hq,
-                       Hkv, max_splits, split_len, (uint16_t*)out, ldo);
+                       (const float*)w.ml, kv_lens, cap, Hq, Hkv, max_splits, split_len, (uint16_t*)out, ldo);
     return bi_launch_status();
 }
 

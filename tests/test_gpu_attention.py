@@ -192,6 +192,31 @@ def test_prefill_varlen_batch_invariance(ops):
         assert np.array_equal(batch[q_start[s]:q_start[s + 1]], alone), f"s={s}"
 
 
+def test_decode_empty_sequences_and_one_split_calls(ops):
+    """Sequences with no token (kv_len 0 or negative) get a zero output, and a
+    call whose max_kv_len fits one split (the combine kernel is not launched)
+    gives the same bits as the same work with a larger max_kv_len (combine
+    launched, every sequence still one split), and as each sequence alone."""
+    g = np.random.default_rng(21)
+    lens = np.array([0, 5, 0, 200, -3], np.int32)
+    kvs = [I.kv_sequence(I.TAG_DECODE, 21, s, max(1, int(l))) for s, l in enumerate(lens)]
+    cache, table = make_cache(g, kvs, capacities=[300] * len(lens))
+    q = I.queries(I.TAG_DECODE, 21, len(lens))
+    outs = []
+    for max_len in (200, 300):
+        log(f"decode empty sequences max_kv_len={max_len}")
+        out = torch.full((len(lens), HQ, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        ops.bi_attention_decode(dev_bf16(q), cache.k, cache.v, dev_i32(table), dev_i32(lens), max_len, SCALE,
+                                out=out)
+        outs.append(host_bits(out))
+    assert np.array_equal(outs[0], outs[1])
+    for s in (0, 2, 4):
+        assert np.all(outs[0][s] == 0), f"sequence {s} (no token) must be zero"
+    for s in (1, 3):
+        alone = decode(ops, cache, table[s:s + 1], q[s:s + 1], lens[s:s + 1])
+        assert np.array_equal(outs[0][s], alone[0]), f"s={s}"
+
+
 def test_decode_long_sequences_fold_over_chunks(ops, orc):
     """Sequences longer than 128 splits (the combine folds them 128 at a time):
     decode equals the prefill row at the same length bit for bit, and matches
