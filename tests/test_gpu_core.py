@@ -246,6 +246,42 @@ def test_matmul_tile_edges_equal_bits(ops, orc):
         check_bf16(full[rows], orc.matmul_f64(x[rows], wt), f"matmul edges N={N} K={K}")
 
 
+# the toy decoder's projections: QKV, O, gate|up, down, and the fp32 output head
+TOY_GEMMS = ((3072, 2048, "bf16"), (2048, 2048, "bf16"), (11264, 2048, "bf16"), (2048, 5632, "bf16"),
+             (32000, 2048, "f32"))
+
+
+@pytest.mark.parametrize("N,K,out", TOY_GEMMS)
+def test_matmul_toy_shapes_parity_and_batch_invariance(ops, orc, N, K, out):
+    """The GEMMs of the toy decoder's step at the token counts its steps see
+    (1 to a few hundred rows): every row of a batch of M equals the same row
+    inside a 600-row batch, bit for bit, and sampled rows match the oracle
+    (bf16 outputs to the bf16 bar, the fp32 head to 1e-2 of the row RMS)."""
+    g = np.random.default_rng(N + K)
+    x = I.normal_bf16(g, (600, K))
+    wt = I.normal_bf16(g, (N, K), 0, 0.02)
+    xd, wd = dev_bf16(x), dev_bf16(wt)
+    f32 = out == "f32"
+    log(f"matmul toy shape N={N} K={K} out={out}")
+
+    def run(a):
+        if f32:
+            return ops.bi_matmul(a, wd, out_dtype=torch.float32).cpu().numpy().view(np.uint32)
+        return host_bits(ops.bi_matmul(a, wd))
+    full = run(xd)
+    for M in (1, 5, 40, 64, 65, 300):
+        assert np.array_equal(run(xd[:M]), full[:M]), f"M={M}"
+        assert np.array_equal(run(xd[600 - M:]), full[600 - M:]), f"last M={M}"
+    rows = [0, 1, 64, 299, 599]
+    ref = orc.matmul_f64(x[rows], wt)
+    if f32:
+        got = full[rows].view(np.float32).astype(np.float64)
+        bound = 1e-2 * np.sqrt(np.mean(ref ** 2, axis=1, keepdims=True))
+        assert np.all(np.abs(got - ref) <= bound)
+    else:
+        check_bf16(full[rows], ref, f"matmul toy shape N={N} K={K}")
+
+
 def test_matmul_repeat_bitwise(ops):
     g = np.random.default_rng(9)
     a = dev_bf16(I.normal_bf16(g, (333, 2048)))
