@@ -186,6 +186,28 @@ def test_matmul_tiny_chain_parity_and_invariance(ops, orc):
         assert np.array_equal(c[0], ref0)
 
 
+def test_tiny_chain_fixed_row_at_every_position(ops):
+    """The tiny configuration's fixed row placed at every position p < B of a
+    batch of B (the other rows random): its RMSNorm output, rstd and matmul row
+    equal, bit for bit, those of the batch of 1 that holds it alone."""
+    w, wt = I.tiny_weights()
+    wd, wtd = dev_bf16(w), dev_bf16(wt)
+    row = I.tiny_x(1)[0]
+    y1, r1 = ops.bi_rmsnorm(dev_bf16(row[None]), wd, I.TINY_EPS)
+    c1 = host_bits(ops.bi_matmul(y1, wtd))[0]
+    y1b, r1b = host_bits(y1)[0], r1.cpu().numpy().view(np.uint32)[0]
+    for B in (2, 3, 8):
+        x = I.tiny_x(B, trial=7)
+        for p in range(B):
+            xb = x.copy()
+            xb[p] = row
+            y, r = ops.bi_rmsnorm(dev_bf16(xb), wd, I.TINY_EPS)
+            c = host_bits(ops.bi_matmul(y, wtd))
+            assert np.array_equal(host_bits(y)[p], y1b), f"B={B} p={p}"
+            assert r.cpu().numpy().view(np.uint32)[p] == r1b, f"B={B} p={p}"
+            assert np.array_equal(c[p], c1), f"B={B} p={p}"
+
+
 @pytest.mark.parametrize("N", list(I.LLAMA_N))
 def test_matmul_llama_parity_sampled(ops, orc, N):
     wt = I.llama_weight(N)
