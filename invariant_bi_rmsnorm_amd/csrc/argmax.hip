@@ -5,11 +5,15 @@
 // One workgroup per row.  (value, index) pairs combine by "larger value wins,
 // equal values keep the lower index", an associative and commutative rule, so
 // the chosen index never depends on the reduction order; a NaN anywhere gives -1.
+// 1024 threads per row, each with kUnroll independent loads in flight (a
+// decoding step has few rows, so each row's scan is latency-bound).
 #include "bi_common.hpp"
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 8;
 
 __device__ __forceinline__ void better(float& v, int& i, float v2, int i2)
 {
@@ -19,18 +23,31 @@ __device__ __forceinline__ void better(float& v, int& i, float v2, int i2)
 __global__ __launch_bounds__(kThreads) void argmax_kernel(const float* __restrict__ x, int64_t ld,
                                                           int64_t V, int32_t* __restrict__ ids)
 {
-    __shared__ float s_v[4];
-    __shared__ int s_i[4];
-    __shared__ int s_nan[4];
+    __shared__ float s_v[kWaves];
+    __shared__ int s_i[kWaves];
+    __shared__ int s_nan[kWaves];
     const int64_t r = blockIdx.x;
     const float* row = x + r * ld;
     float bv = 0.0f;
     int bi = -1;
     int nan = 0;
-    for (int64_t j = threadIdx.x; j < V; j += kThreads) {
-        const float v = row[j];
-        if (v != v) nan = 1;
-        else if (bi < 0 || v > bv) { bv = v; bi = (int)j; }
+    // this thread's entries in increasing index order (a strict > keeps the
+    // lowest index among its equal values)
+    for (int64_t j0 = threadIdx.x; j0 < V; j0 += (int64_t)kThreads * kUnroll) {
+        float v[kUnroll];
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const int64_t j = j0 + (int64_t)k * kThreads;
+            v[k] = j < V ? row[j] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const int64_t j = j0 + (int64_t)k * kThreads;
+            if (j < V) {
+                if (v[k] != v[k]) nan = 1;
+                else if (bi < 0 || v[k] > bv) { bv = v[k]; bi = (int)j; }
+            }
+        }
     }
     for (int off = 32; off >= 1; off >>= 1) {
         const float v2 = __shfl_xor(bv, off, 64);
@@ -45,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(const float* __restric
         float v = s_v[0];
         int i = s_i[0];
         int n = s_nan[0];
-        for (int k = 1; k < 4; ++k) { better(v, i, s_v[k], s_i[k]); n |= s_nan[k]; }
+        for (int k = 1; k < kWaves; ++k) { better(v, i, s_v[k], s_i[k]); n |= s_nan[k]; }
         ids[r] = n ? -1 : i;
     }
 }

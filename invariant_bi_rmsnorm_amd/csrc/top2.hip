@@ -7,7 +7,9 @@
 // largest logit at any other index (a tie gives 0), one fp32 subtraction;
 // V == 1 gives +inf; a NaN gives id -1 and margin NaN.
 //
-// One row per 256-thread workgroup.  A thread keeps (top1 value, its index,
+// One row per 1024-thread workgroup (each thread with kUnroll independent
+// loads in flight: a decoding step has few rows, so a row's scan is
+// latency-bound).  A thread keeps (top1 value, its index,
 // top2 value); two such triples merge as: top1 = the better of the two top1s
 // (larger value, equal values keep the lower index), top2 = the largest of the
 // other top1 and both top2s.  Every piece is a maximum or a total-order choice,
@@ -16,7 +18,8 @@
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
+constexpr int kUnroll = 8;
 
 struct Top2 {
     float v1;
@@ -45,10 +48,21 @@ __global__ __launch_bounds__(kThreads) void top2_kernel(const float* __restrict_
     const float* row = x + (int64_t)blockIdx.x * ld;
     Top2 a{-INFINITY, -1, -INFINITY};
     int nan = 0;
-    for (int i = t; i < V; i += kThreads) {
-        const float v = row[i];
-        if (v != v) nan = 1;
-        else a = merge(a, Top2{v, i, -INFINITY});
+    for (int64_t i0 = t; i0 < V; i0 += (int64_t)kThreads * kUnroll) {
+        float v[kUnroll];
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const int64_t i = i0 + (int64_t)k * kThreads;
+            v[k] = i < V ? row[i] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const int64_t i = i0 + (int64_t)k * kThreads;
+            if (i < V) {
+                if (v[k] != v[k]) nan = 1;
+                else a = merge(a, Top2{v[k], (int)i, -INFINITY});
+            }
+        }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {

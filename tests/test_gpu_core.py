@@ -315,13 +315,22 @@ def test_matmul_repeat_bitwise(ops):
 
 # ------------------------------------------------------------------ argmax
 
-def test_argmax_matches_oracle(ops, orc):
-    g = np.random.default_rng(5)
-    x = g.standard_normal((40, 32000)).astype(np.float32)
-    for r in range(0, 40, 4):
-        i, j = sorted(g.choice(32000, 2, replace=False))
-        x[r, i] = x[r, j] = x[r].max() + 1.0
-    x[13, 777] = np.nan
+@pytest.mark.parametrize("V", [1, 2, 1023, 1025, 8193, 32000, 70001])
+def test_argmax_matches_oracle(ops, orc, V):
+    """Planted ties (the lowest index must win) at random positions, at
+    positions one thread reads in one unrolled group (1024 apart) and in two
+    of its iterations (8192 apart); a NaN row gives -1."""
+    g = np.random.default_rng(5 + V)
+    x = g.standard_normal((40, V)).astype(np.float32)
+    if V > 1:
+        for r in range(0, 40, 4):
+            i, j = sorted(g.choice(V, 2, replace=False))
+            x[r, i] = x[r, j] = x[r].max() + 1.0
+        for r, d in ((1, 1024), (2, 8192)):
+            if V > d:
+                i = int(g.integers(0, V - d))
+                x[r, i] = x[r, i + d] = x[r].max() + 1.0
+    x[13, V // 2] = np.nan
     ids = ops.bi_argmax(torch.from_numpy(x).cuda()).cpu().numpy()
     assert np.array_equal(ids, orc.argmax(x))
     assert ids[13] == -1
