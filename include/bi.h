@@ -163,6 +163,9 @@ size_t bi_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D, int32_t ma
  * q [S rows][ldq] bf16, row s holds Hq heads of D; out likewise with ldo.
  * block_table [S][max_blocks] int32 physical block ids; kv_lens [S] int32 in
  * [1, max_kv_len] and <= max_blocks*16.  scale multiplies q.k (1/sqrt(D) usually).
+ * kv_lens live on the device and are not checked on the host: a length of 0
+ * or less gives that sequence an all-zero output row, and a length past the
+ * limits is cut to min(max_blocks*16, max_kv_len rounded up to 256).
  * A block id outside [0, num_blocks) names no block: its 16 tokens take no part
  * in the attention (score -inf, value 0), here and in bi_attention_prefill
  * alike, so such a row still does not depend on the rest of the batch (a row
