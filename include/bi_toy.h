@@ -49,6 +49,17 @@ int bi_rope(void* x, int64_t ldx, int32_t H, int32_t D, const int32_t* pos, int6
 /* out = bf16(a + b), n bf16 elements (n % 8 == 0); out may alias a or b. */
 int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream);
 
+/* A pre-norm decoder's residual add and the RMSNorm after it, in one launch:
+ * for each of the M rows, h[m] <- bf16(h[m] + r[m]) element by element, then
+ * y[m] = bi_rmsnorm of the new h[m] (rstd[m] as there, when rstd is not NULL).
+ * The bits equal those of bi_add followed by bi_rmsnorm (the RMSNorm of
+ * include/bi.h, table row RMSNorm of the post 論文／ブログ「Defeating
+ * Nondeterminism in LLM Inference」の技術的なポイント); the same requirements
+ * as bi_rmsnorm apply to h (as x), w, y and H, and r [M][ldr] is laid out like
+ * h; y must not be h (BI_ERR_INVALID_ARGUMENT).  Device pointers. */
+int bi_add_rmsnorm(void* h, int64_t ldh, const void* r, int64_t ldr, const void* w, void* y, int64_t ldy,
+                   float* rstd, int64_t M, int64_t H, float eps, void* stream);
+
 /* out[t][j] = bf16( silu(gu[t][j]) * gu[t][F + j] ), silu(g) = g / (1 + exp(-g)),
  * fp32 arithmetic; gu [T][ldgu] holds gate | up.  Requires F % 8 == 0. */
 int bi_silu_mul(const void* gu, int64_t ldgu, int64_t F, void* out, int64_t ldo, int64_t T,

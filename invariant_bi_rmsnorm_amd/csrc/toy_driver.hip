@@ -15,7 +15,9 @@
 // Per layer: RMSNorm -> QKV matmul -> RoPE on q,k -> KV append -> attention
 // (decode kernel for the single-token sequences, prefill kernel for the
 // chunks; both give the same bits for the same row) -> O matmul -> residual ->
-// RMSNorm -> gate|up matmul -> SiLU*mul -> down matmul -> residual.
+// RMSNorm -> gate|up matmul -> SiLU*mul -> down matmul -> residual.  Each
+// residual add that an RMSNorm follows runs in the same launch as that
+// RMSNorm (bi_add_rmsnorm: the same bits as the two calls).
 // Then the last row of each sequence (and any further rows the step asks for):
 // RMSNorm -> LM head (fp32 logits) -> [rows with a small top-2 margin: the head
 // again in fp32 from the unrounded norm, when asked] -> argmax.
@@ -122,7 +124,11 @@ extern "C" int bi_toy_step(const bi_toy_config* c, const bi_toy_weights* w, cons
     CHECK(bi_embed(w->embed, V, H, st->ids, T, h, H, stream));
     for (int l = 0; l < c->layers; ++l) {
         const void* const* lw = w->layer + 6 * l;
-        CHECK(bi_rmsnorm(h, H, lw[0], xn, H, nullptr, T, H, c->eps, stream));
+        // (from the second layer on, with the previous layer's MLP residual add)
+        if (l == 0)
+            CHECK(bi_rmsnorm(h, H, lw[0], xn, H, nullptr, T, H, c->eps, stream));
+        else
+            CHECK(bi_add_rmsnorm(h, H, tmp, H, lw[0], xn, H, nullptr, T, H, c->eps, stream));
         CHECK(bi_matmul(xn, H, lw[1], H, qkv, QKV, BI_BF16, T, QKV, H, stream));
         CHECK(bi_rope(qkv, QKV, Hq + Hkv, (int32_t)D, st->pos, T, w->rope_table, c->max_pos, stream));
         CHECK(bi_kv_append(qkv + (int64_t)Hq * D, qkv + (int64_t)(Hq + Hkv) * D, QKV, st->slots, T,
@@ -140,13 +146,12 @@ extern "C" int bi_toy_step(const bi_toy_config* c, const bi_toy_weights* w, cons
                                        scale, stream));
         CHECK(bi_matmul(attn, (int64_t)Hq * D, lw[2], (int64_t)Hq * D, tmp, H, BI_BF16, T, H,
                         (int64_t)Hq * D, stream));
-        CHECK(bi_add(h, tmp, h, T * H, stream));
-        CHECK(bi_rmsnorm(h, H, lw[3], xn, H, nullptr, T, H, c->eps, stream));
+        CHECK(bi_add_rmsnorm(h, H, tmp, H, lw[3], xn, H, nullptr, T, H, c->eps, stream));
         CHECK(bi_matmul(xn, H, lw[4], H, gu, 2 * F, BI_BF16, T, 2 * F, H, stream));
         CHECK(bi_silu_mul(gu, 2 * F, F, act, F, T, stream));
         CHECK(bi_matmul(act, F, lw[5], F, tmp, H, BI_BF16, T, H, F, stream));
-        CHECK(bi_add(h, tmp, h, T * H, stream));
     }
+    CHECK(bi_add(h, tmp, h, T * H, stream));          // the last layer's MLP residual
     CHECK(bi_gather_rows(h, H, T, st->logit_rows, R, H, hl, H, stream));
     CHECK(bi_rmsnorm(hl, H, w->final_norm, xl, H, nullptr, R, H, c->eps, stream));
     CHECK(bi_matmul(xl, H, w->lm_head, H, logits, V, BI_F32, R, V, H, stream));

@@ -67,6 +67,7 @@ SIGNATURES = {
     "bi_rope_table": (ctypes.c_int, [_P, _I32, _I32, ctypes.c_double, _P]),
     "bi_rope": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I64, _P, _I32, _P]),
     "bi_add": (ctypes.c_int, [_P, _P, _P, _I64, _P]),
+    "bi_add_rmsnorm": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I64, _F, _P]),
     "bi_silu_mul": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _P]),
     "bi_gather_rows": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P]),
     "bi_toy_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32]),
@@ -550,6 +551,23 @@ def bi_add(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor = None, stream=No
     _need_dense(out, torch.bfloat16, tuple(a.shape), "out")
     _check(lib().bi_add(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)), "bi_add")
     return out
+
+
+def bi_add_rmsnorm(h: torch.Tensor, r: torch.Tensor, w: torch.Tensor, eps: float, y: torch.Tensor = None,
+                   want_rstd: bool = True, stream=None):
+    """h [M, H] <- bf16(h + r) in place, then (y, rstd) = RMSNorm of the new h."""
+    M, H = h.shape
+    _need_dense(h, torch.bfloat16, (M, H), "h")
+    _need_dense(r, torch.bfloat16, (M, H), "r")
+    _need_dense(w, torch.bfloat16, (H,), "w")
+    if y is None:
+        y = torch.empty_like(h)
+    _need_dense(y, torch.bfloat16, (M, H), "y")
+    rstd = torch.empty((M,), dtype=torch.float32, device=h.device) if want_rstd else None
+    _check(lib().bi_add_rmsnorm(_ptr(h), _ld(h), _ptr(r), _ld(r), _ptr(w), _ptr(y), _ld(y),
+                                _ptr(rstd) if rstd is not None else None, M, H, float(eps), _stream(stream)),
+           "bi_add_rmsnorm")
+    return y, rstd
 
 
 def bi_silu_mul(gu: torch.Tensor, out: torch.Tensor = None, stream=None):

@@ -193,6 +193,17 @@ def test_probe_copy_validation(L):
     assert L.bi_probe_copy(MIS, A16, 32, None) == 1
 
 
+def test_add_rmsnorm_validation(L):
+    f = L.bi_add_rmsnorm
+    assert f(A16, 64, A16, 64, A16, A16 + 4096, 64, None, 0, 64, 1e-6, None) == 0      # M == 0: no-op
+    assert f(A16, 64, A16, 63, A16, A16 + 4096, 64, None, 2, 64, 1e-6, None) == 1      # ldr < H
+    assert f(A16, 64, None, 64, A16, A16 + 4096, 64, None, 2, 64, 1e-6, None) == 1     # no r
+    assert f(A16, 64, MIS, 64, A16, A16 + 4096, 64, None, 2, 64, 1e-6, None) == 1      # misaligned r
+    assert f(A16, 64, A16, 64, A16, A16, 64, None, 2, 64, 1e-6, None) == 1             # y == h
+    assert f(A16, 64, A16, 64, A16, A16 + 4096, 64, None, 2, 60, 1e-6, None) == 2      # H % 8
+    assert f(A16, 64, A16, 64, A16, A16 + 4096, 64, None, 2, 64, -1.0, None) == 1      # eps < 0
+
+
 def test_probe_read_and_lds_fill_validation(L):
     assert L.bi_probe_read(A16, 0, A16, None) == 0
     assert L.bi_probe_read(A16, 17, A16, None) == 1

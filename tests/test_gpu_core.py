@@ -127,6 +127,29 @@ def test_rmsnorm_llama_parity_and_batch_invariance(ops, orc):
         assert np.array_equal(yb[0], ref0[0]) and np.array_equal(rb[:1].view(np.uint32), ref0[1])
 
 
+@pytest.mark.parametrize("M,H", [(1, 2048), (31, 2048), (32, 4096), (77, 256), (300, 16384)])
+def test_add_rmsnorm_equals_add_then_rmsnorm(ops, M, H):
+    """The fused residual add + RMSNorm gives the bits of bi_add then
+    bi_rmsnorm (new residual, normalised row and rstd), in both libraries
+    (the non-invariant build's own RMSNorm order below 32 rows included)."""
+    g = np.random.default_rng(M * 31 + H)
+    h = I.normal_bf16(g, (M, H))
+    r = I.normal_bf16(g, (M, H), 0, 0.5)
+    w = I.normal_bf16(g, (H,), 1.0, 0.1)
+    for path in (ops.DEFAULT_LIB_PATH, ops.NB_LIB_PATH):
+        prev = ops.use_library(path)
+        try:
+            hd, rd, wd = dev_bf16(h), dev_bf16(r), dev_bf16(w)
+            s_ = ops.bi_add(hd, rd)
+            y1, r1 = ops.bi_rmsnorm(s_, wd, 1e-6)
+            y2, r2 = ops.bi_add_rmsnorm(hd, rd, wd, 1e-6)
+            assert np.array_equal(host_bits(hd), host_bits(s_)), f"{path} M={M} H={H}: residual"
+            assert np.array_equal(host_bits(y2), host_bits(y1)), f"{path} M={M} H={H}: output"
+            assert np.array_equal(r2.cpu().numpy().view(np.uint32), r1.cpu().numpy().view(np.uint32))
+        finally:
+            ops.use_library(prev)
+
+
 def test_rmsnorm_row_position_inplace_strided_and_repeat(ops):
     g = np.random.default_rng(7)
     M, H = 300, 4096
