@@ -46,6 +46,19 @@ int bi_rope_table(float* table, int32_t max_pos, int32_t D, double theta, void* 
 int bi_rope(void* x, int64_t ldx, int32_t H, int32_t D, const int32_t* pos, int64_t T,
             const float* table, int32_t max_pos, void* stream);
 
+/* bi_rope on the q and k heads of a fused projection and bi_kv_append of its
+ * k and v heads, in one launch, with the same bits as the two calls in turn:
+ * row t of qkv [T][ld] holds Hq q heads, Hkv k heads and Hkv v heads of D;
+ * the q and k heads are rotated in place (position pos[t], table as in
+ * bi_rope), then k and v are written to k_cache [num_blocks][Hkv][16][D] and
+ * v_cache [num_blocks][Hkv][D][16] at slot slots[t] (the cache layout of
+ * include/bi.h, one layout for cached and fresh tokens; a slot outside the
+ * pool writes no cache entry).  Requires D == 128, ld >= (Hq + 2 Hkv) D,
+ * ld % 8 == 0, 16-byte aligned qkv and caches.  Device pointers. */
+int bi_rope_kv_append(void* qkv, int64_t ld, int32_t Hq, int32_t Hkv, int32_t D, const int32_t* pos,
+                      const int32_t* slots, int64_t T, const float* table, int32_t max_pos, void* k_cache,
+                      void* v_cache, int64_t num_blocks, void* stream);
+
 /* out = bf16(a + b), n bf16 elements (n % 8 == 0); out may alias a or b. */
 int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream);
 

@@ -12,7 +12,7 @@
 // (weights, per-layer paged KV caches, the step description, the workspace);
 // the driver keeps no state between calls and allocates nothing.
 //
-// Per layer: RMSNorm -> QKV matmul -> RoPE on q,k -> KV append -> attention
+// Per layer: RMSNorm -> QKV matmul -> RoPE on q,k and KV append (one launch) -> attention
 // (decode kernel for the single-token sequences, prefill kernel for the
 // chunks; both give the same bits for the same row) -> O matmul -> residual ->
 // RMSNorm -> gate|up matmul -> SiLU*mul -> down matmul -> residual.  Each
@@ -130,9 +130,8 @@ extern "C" int bi_toy_step(const bi_toy_config* c, const bi_toy_weights* w, cons
         else
             CHECK(bi_add_rmsnorm(h, H, tmp, H, lw[0], xn, H, nullptr, T, H, c->eps, stream));
         CHECK(bi_matmul(xn, H, lw[1], H, qkv, QKV, BI_BF16, T, QKV, H, stream));
-        CHECK(bi_rope(qkv, QKV, Hq + Hkv, (int32_t)D, st->pos, T, w->rope_table, c->max_pos, stream));
-        CHECK(bi_kv_append(qkv + (int64_t)Hq * D, qkv + (int64_t)(Hq + Hkv) * D, QKV, st->slots, T,
-                           w->k_cache[l], w->v_cache[l], w->num_blocks, Hkv, (int32_t)D, stream));
+        CHECK(bi_rope_kv_append(qkv, QKV, Hq, Hkv, (int32_t)D, st->pos, st->slots, T, w->rope_table, c->max_pos,
+                                w->k_cache[l], w->v_cache[l], w->num_blocks, stream));
         if (nd > 0)
             CHECK(bi_attention_decode(qkv, QKV, w->k_cache[l], w->v_cache[l], w->num_blocks,
                                       st->block_table, st->max_blocks, st->kv_lens, attn, (int64_t)Hq * D,

@@ -59,6 +59,56 @@ __global__ void rope_kernel(uint16_t* __restrict__ x, int64_t ldx, int D, const 
     }
 }
 
+// Rotary embedding of q and k and the paged-cache append of k and v for one
+// token per workgroup: the q heads are rotated in place; each k pair is
+// rotated in registers, written back and written to the K cache; v is copied
+// to the dim-major V cache.  The rotation is rope_kernel's arithmetic, the
+// cache layout bi_kv_append's (k_cache [blocks][Hkv][16][D], v_cache
+// [blocks][Hkv][D][16]); a slot outside the pool writes no cache entry.
+constexpr int kRopeAppendThreads = 256;
+__global__ __launch_bounds__(kRopeAppendThreads) void rope_kv_append_kernel(
+    uint16_t* __restrict__ qkv, int64_t ld, int Hq, int Hkv, int D, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ slots, const float* __restrict__ table, int max_pos,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int64_t num_blocks)
+{
+    const int64_t t = blockIdx.x;
+    const int half = D >> 1;
+    int p = pos[t];
+    if (p < 0 || p >= max_pos) p = 0;
+    const int64_t slot = slots[t];
+    const bool cached = slot >= 0 && slot < num_blocks * 16;
+    const int64_t blk = slot >> 4;
+    const int off = (int)(slot & 15);
+    uint16_t* row = qkv + t * ld;
+    const float* tab = table + 2 * (int64_t)p * half;
+    // q heads 0..Hq-1 and k heads Hq..Hq+Hkv-1: pair i of head h
+    for (int e = threadIdx.x; e < (Hq + Hkv) * half; e += kRopeAppendThreads) {
+        const int h = e / half;
+        const int i = e - h * half;
+        const float c = tab[2 * i];
+        const float sn = tab[2 * i + 1];
+        uint16_t* r = row + (int64_t)h * D;
+        const float a = bf16_to_f32(r[i]);
+        const float b = bf16_to_f32(r[i + half]);
+        const uint16_t ra = (uint16_t)f32_to_bf16_rne(a * c - b * sn);
+        const uint16_t rb = (uint16_t)f32_to_bf16_rne(b * c + a * sn);
+        r[i] = ra;
+        r[i + half] = rb;
+        if (h >= Hq && cached) {
+            uint16_t* kd = kc + ((blk * Hkv + (h - Hq)) * 16 + off) * D;
+            kd[i] = ra;
+            kd[i + half] = rb;
+        }
+    }
+    if (!cached) return;
+    const uint16_t* v = row + (int64_t)(Hq + Hkv) * D;
+    for (int e = threadIdx.x; e < Hkv * D; e += kRopeAppendThreads) {
+        const int h = e / D;
+        const int d = e - h * D;
+        vc[((blk * Hkv + h) * D + d) * 16 + off] = v[e];
+    }
+}
+
 __global__ void add_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
                            uint16_t* __restrict__ out, int64_t n8)
 {
@@ -131,6 +181,27 @@ extern "C" int bi_rope_table(float* table, int32_t max_pos, int32_t D, double th
     const int64_t n = (int64_t)max_pos * (D / 2);
     hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        (hipStream_t)stream, table, max_pos, D / 2, D, theta);
+    return bi_launch_status();
+    BI_TRY_END
+}
+
+extern "C" int bi_rope_kv_append(void* qkv, int64_t ld, int32_t Hq, int32_t Hkv, int32_t D, const int32_t* pos,
+                                 const int32_t* slots, int64_t T, const float* table, int32_t max_pos,
+                                 void* k_cache, void* v_cache, int64_t num_blocks, void* stream)
+{
+    BI_TRY_BEGIN
+    if (T < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_pos <= 0 || num_blocks <= 0 ||
+        ld < (int64_t)(Hq + 2 * Hkv) * D || (ld % 8))
+        return BI_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!qkv || !pos || !slots || !table || !k_cache || !v_cache)) return BI_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!bi_aligned(qkv, 16) || !bi_aligned(k_cache, 16) || !bi_aligned(v_cache, 16) ||
+                  !bi_aligned(pos, 4) || !bi_aligned(slots, 4) || !bi_aligned(table, 4)))
+        return BI_ERR_INVALID_ARGUMENT;
+    if (D != BI_HEAD_DIM || Hq + Hkv > 65535 || T > 0x7fffffffLL) return BI_ERR_UNSUPPORTED;
+    if (T == 0) return BI_OK;
+    hipLaunchKernelGGL(rope_kv_append_kernel, dim3((unsigned)T), dim3(kRopeAppendThreads), 0, (hipStream_t)stream,
+                       (uint16_t*)qkv, ld, Hq, Hkv, D, pos, slots, table, max_pos, (uint16_t*)k_cache,
+                       (uint16_t*)v_cache, num_blocks);
     return bi_launch_status();
     BI_TRY_END
 }

@@ -66,6 +66,7 @@ SIGNATURES = {
     "bi_embed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "bi_rope_table": (ctypes.c_int, [_P, _I32, _I32, ctypes.c_double, _P]),
     "bi_rope": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I64, _P, _I32, _P]),
+    "bi_rope_kv_append": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _P, _P, _I64, _P, _I32, _P, _P, _I64, _P]),
     "bi_add": (ctypes.c_int, [_P, _P, _P, _I64, _P]),
     "bi_add_rmsnorm": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I64, _F, _P]),
     "bi_silu_mul": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _P]),
@@ -551,6 +552,20 @@ def bi_add(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor = None, stream=No
     _need_dense(out, torch.bfloat16, tuple(a.shape), "out")
     _check(lib().bi_add(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)), "bi_add")
     return out
+
+
+def bi_rope_kv_append(qkv: torch.Tensor, Hq: int, Hkv: int, pos: torch.Tensor, slots: torch.Tensor,
+                      table: torch.Tensor, max_pos: int, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      stream=None):
+    """qkv [T, >= (Hq + 2 Hkv) D]: q and k heads rotated in place, k and v
+    appended to the paged cache at slots."""
+    T, D = qkv.shape[0], k_cache.shape[-1]
+    _need(qkv, torch.bfloat16, "qkv")
+    _need_dense(pos, torch.int32, (T,), "pos")
+    _need_dense(slots, torch.int32, (T,), "slots")
+    _check(lib().bi_rope_kv_append(_ptr(qkv), _ld(qkv), Hq, Hkv, D, _ptr(pos), _ptr(slots), T, _ptr(table),
+                                   int(max_pos), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _stream(stream)),
+           "bi_rope_kv_append")
 
 
 def bi_add_rmsnorm(h: torch.Tensor, r: torch.Tensor, w: torch.Tensor, eps: float, y: torch.Tensor = None,

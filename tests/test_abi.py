@@ -193,6 +193,19 @@ def test_probe_copy_validation(L):
     assert L.bi_probe_copy(MIS, A16, 32, None) == 1
 
 
+def test_rope_kv_append_validation(L):
+    f = L.bi_rope_kv_append
+    ld = (16 + 2 * 4) * 128
+    ok = (A16, ld, 16, 4, 128, A16, A16, 3, A16, 64, A16, A16, 10, None)
+    assert f(*ok[:7], 0, *ok[8:]) == 0                                    # T == 0: no-op
+    assert f(A16, ld - 8, *ok[2:]) == 1                                    # ld too small
+    assert f(A16, ld + 4, *ok[2:]) == 1                                    # ld % 8
+    assert f(MIS, *ok[1:]) == 1                                            # misaligned qkv
+    assert f(*ok[:5], None, *ok[6:]) == 1                                  # no positions
+    assert f(*ok[:4], 64, *ok[5:]) == 2                                    # D != 128
+    assert f(*ok[:12], 0, None) == 1                                       # empty pool
+
+
 def test_add_rmsnorm_validation(L):
     f = L.bi_add_rmsnorm
     assert f(A16, 64, A16, 64, A16, A16 + 4096, 64, None, 0, 64, 1e-6, None) == 0      # M == 0: no-op

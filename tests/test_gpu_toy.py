@@ -81,6 +81,37 @@ def test_toy_ops_parity(ops, orc):
     check_bf16(s, I.bf16_to_f32(sr).astype(np.float64), "silu_mul")
 
 
+def test_rope_kv_append_equals_rope_then_append(ops):
+    """The fused rotary embedding + cache append gives the bits of bi_rope on
+    the q and k heads followed by bi_kv_append of k and v: the rotated
+    projection and both caches, with slots outside the pool (no cache write)
+    and positions outside the table (position 0)."""
+    from gpu_util import PagedCache
+    g = np.random.default_rng(17)
+    T, Hq, Hkv, D, nblk = 45, 16, 4, 128, 8
+    qkv = I.normal_bf16(g, (T, (Hq + 2 * Hkv) * D))
+    pos = g.integers(0, 1000, T).astype(np.int32)
+    pos[3], pos[4] = -1, 5000
+    slots = g.permutation(nblk * 16)[:T].astype(np.int32)
+    slots[7], slots[8] = -1, nblk * 16
+    tab = ops.bi_rope_table(1024, D, 10000.0)
+    results = []
+    for fused in (False, True):
+        x = dev_bf16(qkv)
+        cache = PagedCache(nblk, Hkv)
+        cache.k.fill_(float("nan"))
+        cache.v.fill_(float("nan"))
+        if fused:
+            ops.bi_rope_kv_append(x, Hq, Hkv, dev_i32(pos), dev_i32(slots), tab, 1024, cache.k, cache.v)
+        else:
+            xv = x.view(T, Hq + 2 * Hkv, D)
+            ops.bi_rope(xv[:, :Hq + Hkv], dev_i32(pos), tab, 1024)
+            ops.bi_kv_append(xv[:, Hq:Hq + Hkv], xv[:, Hq + Hkv:], dev_i32(slots), cache.k, cache.v)
+        results.append((host_bits(x), host_bits(cache.k), host_bits(cache.v)))
+    for a, b, what in zip(results[0], results[1], ("qkv", "k cache", "v cache")):
+        assert np.array_equal(a, b), what
+
+
 # ------------------------------------------------------------------ first step vs oracle
 
 def test_toy_first_step_logits_parity(ops, orc, toy_weights):
